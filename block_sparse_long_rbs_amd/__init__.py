@@ -1,0 +1,12 @@
+"""MI355X-native RBS block-sparse prefill attention.
+
+The compute lives in librbs.so (hand-written HIP for gfx950, C ABI in
+include/rbs.h); this package holds the ctypes binding, a host-to-device
+upload helper and the seeded synthetic workloads. The shared library is
+loaded on first use; a missing library raises, there is no fallback.
+"""
+from ._lib import (RbsError, block_mask_attn_fwd, blocksparse_attn_fwd, lib, rbs_block_stats,
+                   rbs_select, rbs_select_capacity)
+
+__all__ = ["RbsError", "block_mask_attn_fwd", "blocksparse_attn_fwd", "lib", "rbs_block_stats",
+           "rbs_select", "rbs_select_capacity"]

@@ -1,0 +1,194 @@
+"""ctypes binding of librbs.so (include/rbs.h).
+
+Argument marshalling only: each wrapper checks tensor placement and shapes,
+allocates outputs with torch on the inputs' device, and passes raw device
+pointers plus torch's current HIP stream to the C ABI. Every step of the
+computation runs in the library's HIP kernels. There is no fallback: if the
+shared library is missing, loading fails with an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librbs.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "rbs.h")
+
+RBS_OK, RBS_E_ARG, RBS_E_UNSUPPORTED, RBS_E_CAPACITY, RBS_E_HIP = range(5)
+RBS_DT_BF16, RBS_DT_F32 = 0, 1
+RBS_SEL_FORCE_SINK = 0x1
+
+_c_i32, _c_u32, _c_i64, _c_f32, _c_f64 = (ctypes.c_int32, ctypes.c_uint32, ctypes.c_int64,
+                                          ctypes.c_float, ctypes.c_double)
+_vp = ctypes.c_void_p
+
+_SIGS = {
+    "rbs_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "rbs_block_stats": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
+                                       _c_i32, _vp, _vp, _vp, _vp, _vp]),
+    "rbs_select": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_f64, _c_f64,
+                                  _c_u32, _vp, _vp, _vp, _c_i64, _vp,
+                                  ctypes.POINTER(ctypes.c_size_t), _vp]),
+    "rbs_select_capacity": (_c_i64, [_c_i32, _c_i32, _c_f64, _c_f64, _c_u32]),
+    "blocksparse_attn_fwd": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
+                                            _c_i32, _c_i32, _vp, _vp, _c_f32, _vp, _vp, _vp]),
+    "block_mask_attn_fwd": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
+                                           _c_i32, _c_i32, ctypes.POINTER(_c_i32),
+                                           ctypes.POINTER(_c_i32), _c_f32, _c_i32, _c_f32, _vp,
+                                           _vp, _vp]),
+}
+
+_lib = None
+
+
+class RbsError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load librbs.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m block_sparse_long_rbs_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def declared_symbols() -> list:
+    """Function names declared in include/rbs.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                      text, flags=re.M)
+
+
+def status_string(status: int) -> str:
+    return lib().rbs_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != RBS_OK:
+        raise RbsError(fn, status)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return RBS_DT_BF16
+    if t.dtype == torch.float32:
+        return RBS_DT_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+# ---------------------------------------------------------------------------
+
+def rbs_block_stats(q: torch.Tensor, k: torch.Tensor, block: int):
+    """Per-block centroid, radius, representative query and its norm.
+    q [S, Hq, D], k [S, Hkv, D] (bf16 or f32) -> fp32 (cen [Hkv,nb,D],
+    rad [Hkv,nb], q_rep [Hkv,nb,D], q_rep_norm [Hkv,nb])."""
+    _need_cuda(q, k)
+    S, Hq, D = q.shape
+    Hkv = k.shape[1]
+    nb = -(-S // block)
+    f = dict(device=q.device, dtype=torch.float32)
+    cen, qrep = torch.empty((Hkv, nb, D), **f), torch.empty((Hkv, nb, D), **f)
+    rad, qn = torch.empty((Hkv, nb), **f), torch.empty((Hkv, nb), **f)
+    _check("rbs_block_stats", lib().rbs_block_stats(
+        _dtype_code(q), q.data_ptr(), k.data_ptr(), S, Hq, Hkv, D, block, cen.data_ptr(),
+        rad.data_ptr(), qrep.data_ptr(), qn.data_ptr(), _stream(q)))
+    return cen, rad, qrep, qn
+
+
+def rbs_select_capacity(n_kv_heads: int, n_blocks: int, keep_ratio_centroid: float,
+                        keep_ratio_rescue: float, sink: bool = False) -> int:
+    return int(lib().rbs_select_capacity(n_kv_heads, n_blocks, keep_ratio_centroid,
+                                         keep_ratio_rescue, RBS_SEL_FORCE_SINK if sink else 0))
+
+
+def rbs_select(cen, rad, qrep, qnorm, keep_ratio_centroid: float, keep_ratio_rescue: float,
+               sink: bool = False, beta: Optional[torch.Tensor] = None, want_beta: bool = False,
+               workspace: Optional[torch.Tensor] = None):
+    """Dual-branch selection -> (row_ptr [Hkv*nb+1] int32, col_idx [capacity]
+    int32, beta_used [Hkv,nb] fp32 or None). Only col_idx[:row_ptr[-1]] is
+    meaningful."""
+    _need_cuda(cen, rad, qrep, qnorm, beta)
+    Hkv, nb, D = cen.shape
+    flags = RBS_SEL_FORCE_SINK if sink else 0
+    L = lib()
+    ws = ctypes.c_size_t(0)
+    _check("rbs_select", L.rbs_select(None, None, None, None, None, Hkv, nb, D,
+                                      keep_ratio_centroid, keep_ratio_rescue, flags, None, None,
+                                      None, 0, None, ctypes.byref(ws), None))
+    if workspace is None or workspace.numel() < ws.value:
+        workspace = torch.empty(ws.value, dtype=torch.uint8, device=cen.device)
+    cap = rbs_select_capacity(Hkv, nb, keep_ratio_centroid, keep_ratio_rescue, sink)
+    row_ptr = torch.empty(Hkv * nb + 1, dtype=torch.int32, device=cen.device)
+    col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=cen.device)
+    beta_out = torch.empty((Hkv, nb), dtype=torch.float32, device=cen.device) if want_beta else None
+    wsz = ctypes.c_size_t(workspace.numel())
+    _check("rbs_select", L.rbs_select(
+        cen.data_ptr(), rad.data_ptr(), qrep.data_ptr(), qnorm.data_ptr(), _ptr(beta), Hkv, nb, D,
+        keep_ratio_centroid, keep_ratio_rescue, flags, _ptr(beta_out), row_ptr.data_ptr(),
+        col_idx.data_ptr(), cap, workspace.data_ptr(), ctypes.byref(wsz), _stream(cen)))
+    return row_ptr, col_idx, beta_out
+
+
+def blocksparse_attn_fwd(q, k, v, block: int, row_ptr, col_idx, softmax_scale: float = 0.0,
+                         want_lse: bool = False, out: Optional[torch.Tensor] = None):
+    """Causal GQA attention over the CSR-selected key blocks -> (out, lse or None)."""
+    _need_cuda(q, k, v, row_ptr, col_idx)
+    S, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((Hq, S), dtype=torch.float32, device=q.device) if want_lse else None
+    _check("blocksparse_attn_fwd", lib().blocksparse_attn_fwd(
+        _dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), S, Hq, Hkv, D, block,
+        row_ptr.data_ptr(), col_idx.data_ptr(), softmax_scale, out.data_ptr(), _ptr(lse),
+        _stream(q)))
+    return out, lse
+
+
+def block_mask_attn_fwd(q, k_cached, v, seg_start: Sequence[int], k_rerotate: Sequence[int],
+                        rope_theta: float, q_row_begin: int = 0, softmax_scale: float = 0.0,
+                        want_lse: bool = False, out: Optional[torch.Tensor] = None):
+    """Block-attention prefill with RoPE re-encoding of cached keys -> (out, lse or None)."""
+    _need_cuda(q, k_cached, v)
+    S, Hq, D = q.shape
+    Hkv = k_cached.shape[1]
+    n_seg = len(seg_start) - 1
+    ss = (_c_i32 * (n_seg + 1))(*[int(x) for x in seg_start])
+    rr = (_c_i32 * max(n_seg, 1))(*[int(x) for x in k_rerotate])
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((Hq, S), dtype=torch.float32, device=q.device) if want_lse else None
+    _check("block_mask_attn_fwd", lib().block_mask_attn_fwd(
+        _dtype_code(q), q.data_ptr(), k_cached.data_ptr(), v.data_ptr(), S, Hq, Hkv, D, n_seg, ss,
+        rr, rope_theta, q_row_begin, softmax_scale, out.data_ptr(), _ptr(lse), _stream(q)))
+    return out, lse

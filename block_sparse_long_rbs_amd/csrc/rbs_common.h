@@ -1,0 +1,90 @@
+// Internal helpers shared by the librbs HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/rbs.h"
+
+namespace rbs {
+
+constexpr int kWave = 64;
+
+// bf16 is carried as raw uint16_t bits; widening is a shift.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Round-to-nearest-even float -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  return x;
+}
+
+// Launch-error helper for host launchers.
+inline rbs_status launch_status() {
+  return hipGetLastError() == hipSuccess ? RBS_OK : RBS_E_HIP;
+}
+
+// Host launchers (one per kernel family); arguments are validated by the API layer.
+rbs_status launch_block_stats(rbs_dtype dt, const void* q, const void* k, int S, int Hq, int Hkv,
+                              int D, int B, float* cen, float* rad, float* qrep, float* qnorm,
+                              hipStream_t st);
+
+struct SelectArgs {
+  const float* cen;
+  const float* rad;
+  const float* qrep;
+  const float* qnorm;
+  const float* beta_in;
+  float* beta_out;
+  int32_t* row_ptr;
+  int32_t* col_idx;
+  int32_t* counts;   // workspace: [Hkv*nb]
+  int32_t* lists;    // workspace: [Hkv*nb][stride]
+  int Hkv, nb, D, stride;
+  double rho_c, rho_r;
+  int sink;
+};
+rbs_status launch_select(const SelectArgs& a, hipStream_t st);
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int S, Hq, Hkv, D, B;
+  float scale;
+};
+rbs_status launch_attn_bf16_csr(const AttnArgs& a, hipStream_t st);
+rbs_status launch_attn_f32_csr(const AttnArgs& a, hipStream_t st);
+int select_rows_per_group(int nb, int D);
+
+constexpr int kMaxSegments = 256;
+struct SegArgs {
+  int n_seg;
+  int q_row_begin;
+  float theta;
+  int32_t start[kMaxSegments + 1];
+  int32_t rerot[kMaxSegments];
+};
+rbs_status launch_attn_segments(const AttnArgs& a, const SegArgs& s, hipStream_t st);
+
+}  // namespace rbs

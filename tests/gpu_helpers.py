@@ -1,0 +1,174 @@
+"""Shared helpers for the GPU parity tests: run the HIP path through the
+binding, run the oracle on the same inputs, and compare under the parity
+rules (selected sets exact outside the threshold band; attention within the
+dtype's tolerance)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import block_sparse_long_rbs_amd as rbs
+from block_sparse_long_rbs_amd import device
+from oracle import rbs_oracle as orc
+
+# Attention tolerances: bf16 inputs (max-abs, mean-abs) and fp32 inputs.
+TOL_BF16_MAX, TOL_BF16_MEAN = 2e-2, 1e-2
+TOL_F32 = 1e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_stats(w, t):
+    return [x.cpu().numpy().astype(np.float64) for x in rbs.rbs_block_stats(t["q"], t["k"], w.block)]
+
+
+def gpu_select(w, t, stats_dev):
+    cen, rad, qrep, qn = stats_dev
+    rp, ci, beta = rbs.rbs_select(cen, rad, qrep, qn, w.keep_ratio_centroid, w.keep_ratio_rescue,
+                                  sink=w.sink, beta=t.get("beta"), want_beta=True)
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    ci_h = ci.cpu().numpy()[:rp_h[-1]]
+    return rp, ci, rp_h, ci_h, beta.cpu().numpy()
+
+
+def oracle_selection(w):
+    c, r, qr, qn = orc.block_stats(w.q, w.k, w.n_kv_heads, w.block)
+    beta = w.beta.astype(np.float64) if w.beta is not None else orc.derive_beta(r)
+    sel = orc.select(c, r, qr, qn, beta, w.keep_ratio_centroid, w.keep_ratio_rescue, w.sink)
+    return (c, r, qr, qn), sel
+
+
+def compare_stats(gpu, ora, rel=1e-5):
+    names = ("centroid", "radius", "q_rep", "q_rep_norm")
+    for name, g, o in zip(names, gpu, ora):
+        scale = np.abs(o).max() if o.size else 1.0
+        err = np.abs(g - o).max() if o.size else 0.0
+        assert err <= rel * max(scale, 1e-30), f"{name}: max err {err} vs scale {scale}"
+
+
+def compare_selection(sel, rp_h, ci_h, Hkv, nb, sink):
+    """Sets bit-exact except blocks in the oracle's threshold band. Returns
+    (rows that differ, rows checked)."""
+    differing = 0
+    for r in range(Hkv * nb):
+        i = r % nb
+        got = ci_h[rp_h[r]:rp_h[r + 1]].tolist()
+        assert got == sorted(set(got)), f"row {r} not strictly ascending: {got}"
+        assert got and got[-1] == i, f"row {r} misses its diagonal block"
+        if sink:
+            assert got[0] == 0, f"row {r} misses the sink"
+        want = set(sel.col_idx[sel.row_ptr[r]:sel.row_ptr[r + 1]].tolist())
+        diff = set(got) ^ want
+        if diff:
+            differing += 1
+            assert diff <= sel.exempt[r], (f"row {r}: differs at {sorted(diff)}, "
+                                           f"exempt {sorted(sel.exempt[r])}")
+    return differing, Hkv * nb
+
+
+def attn_errors(gpu_out, ora_out, rows_tokens, heads=None):
+    g = gpu_out[rows_tokens]
+    o = ora_out[rows_tokens]
+    if heads is not None:
+        g, o = g[:, heads], o[:, heads]
+    d = np.abs(g.astype(np.float64) - o)
+    return float(d.max()), float(d.mean())
+
+
+def check_attn(w, gpu_out, ora_out, tokens):
+    mx, mean = attn_errors(gpu_out, ora_out, tokens)
+    if w.dtype == "f32":
+        assert mx <= TOL_F32, f"fp32 attention max-abs {mx}"
+    else:
+        assert mx <= TOL_BF16_MAX and mean <= TOL_BF16_MEAN, f"bf16 attention max {mx} mean {mean}"
+    return mx, mean
+
+
+def csr_to_device(row_ptr, col_idx, dev="cuda"):
+    return (torch.from_numpy(np.asarray(row_ptr, np.int32)).to(dev),
+            torch.from_numpy(np.asarray(col_idx, np.int32)).to(dev))
+
+
+def row_tokens(rows, block, S):
+    toks = []
+    for (_, i) in rows:
+        toks.extend(range(i * block, min(S, (i + 1) * block)))
+    return np.unique(np.asarray(toks, np.int64))
+
+
+def to_host(x: torch.Tensor) -> np.ndarray:
+    return x.float().cpu().numpy().astype(np.float64)
+
+
+def _slab_errors(gpu_out, ora_out, rows, w):
+    G = w.group
+    errs = []
+    for g, i in rows:
+        t0, t1 = i * w.block, min(w.seqlen, (i + 1) * w.block)
+        a = gpu_out[t0:t1, g * G:(g + 1) * G]
+        b = ora_out[t0:t1, g * G:(g + 1) * G]
+        errs.append(np.abs(a - b).reshape(-1))
+    e = np.concatenate(errs)
+    return float(e.max()), float(e.mean())
+
+
+def _assert_attn(w, mx, mean, what):
+    say(f"  {what}: max-abs {mx:.3e} mean-abs {mean:.3e}")
+    if w.dtype == "f32":
+        assert mx <= TOL_F32, f"{what}: fp32 max-abs {mx}"
+    else:
+        assert mx <= TOL_BF16_MAX and mean <= TOL_BF16_MEAN, f"{what}: max {mx} mean {mean}"
+
+
+def pipeline_case(w, sample_rows=None, seed=0):
+    """Full parity for one workload; sample_rows bounds the attention oracle."""
+    say(f"[case] {w.name} S={w.seqlen} Hq={w.n_q_heads} Hkv={w.n_kv_heads} D={w.head_dim} "
+          f"B={w.block} dtype={w.dtype}")
+    t = device.upload(w)
+    stats_dev = rbs.rbs_block_stats(t["q"], t["k"], w.block)
+    torch.cuda.synchronize()
+    gstats = [to_host(x) for x in stats_dev]
+    ostats, sel = oracle_selection(w)
+    compare_stats(gstats, ostats)
+    rp, ci, rp_h, ci_h, beta_g = gpu_select(w, t, stats_dev)
+    if w.beta is None:
+        np.testing.assert_allclose(beta_g, sel.beta, atol=1e-5)
+    nb = w.n_blocks
+    diff, total = compare_selection(sel, rp_h, ci_h, w.n_kv_heads, nb, w.sink)
+    say(f"  selection: {diff}/{total} rows differ, all inside the threshold band")
+    rows = [(g, i) for g in range(w.n_kv_heads) for i in range(nb)]
+    if sample_rows is not None and len(rows) > sample_rows:
+        rng = np.random.default_rng(seed)
+        pick = rng.choice(len(rows), size=sample_rows, replace=False)
+        rows = [rows[k] for k in sorted(pick)] + [(0, 0), (w.n_kv_heads - 1, nb - 1)]
+    # attention on the oracle's CSR
+    rp_o, ci_o = csr_to_device(sel.row_ptr, sel.col_idx)
+    out_g, lse_g = rbs.blocksparse_attn_fwd(t["q"], t["k"], t["v"], w.block, rp_o, ci_o,
+                                            want_lse=True)
+    out_o, lse_o = orc.blocksparse_attention(w.q, w.k, w.v, w.block, sel.row_ptr, sel.col_idx,
+                                             rows=rows)
+    out_gh = to_host(out_g)
+    mx, mean = _slab_errors(out_gh, out_o, rows, w)
+    _assert_attn(w, mx, mean, "attention on oracle CSR")
+    lse_gh = lse_g.cpu().numpy()
+    G = w.group
+    for g, i in rows:
+        t0, t1 = i * w.block, min(w.seqlen, (i + 1) * w.block)
+        d = np.abs(lse_gh[g * G:(g + 1) * G, t0:t1] - lse_o[g * G:(g + 1) * G, t0:t1]).max()
+        assert d <= (1e-5 if w.dtype == "f32" else 2e-2), f"lse row {(g, i)} err {d}"
+    # end to end on rows whose GPU set equals the oracle's
+    out_e, _ = rbs.blocksparse_attn_fwd(t["q"], t["k"], t["v"], w.block, rp, ci)
+    out_eh = to_host(out_e)
+    same = [(g, i) for (g, i) in rows
+            if ci_h[rp_h[g * nb + i]:rp_h[g * nb + i + 1]].tolist() == sel.row(g, i).tolist()]
+    if same:
+        mx, mean = _slab_errors(out_eh, out_o, same, w)
+        _assert_attn(w, mx, mean, f"end to end on {len(same)}/{len(rows)} rows")
+    return dict(t=t, sel=sel, rp=rp, ci=ci, out=out_g)
+
+

@@ -1,0 +1,134 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every
+declared call, and rejects bad arguments on the host before any HIP call.
+
+Pointers passed here are fake (never dereferenced): every case below fails
+validation, which runs before anything touches the device."""
+import ctypes
+
+import pytest
+
+from block_sparse_long_rbs_amd import _lib
+from oracle import rbs_oracle as orc
+
+E = _lib
+P = 0x10000          # fake 16-byte aligned "device" pointer
+PM = 0x10004         # misaligned for 16-byte loads
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = _lib.declared_symbols()
+    assert set(names) >= {"rbs_block_stats", "rbs_select", "blocksparse_attn_fwd",
+                          "block_mask_attn_fwd", "rbs_select_capacity", "rbs_status_string"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    assert _lib.status_string(0) == "ok"
+    assert "argument" in _lib.status_string(1)
+
+
+def stats(L, **kw):
+    a = dict(dt=0, q=P, k=P, S=1024, Hq=8, Hkv=2, D=128, B=128, c=P, r=P, qr=P, qn=P)
+    a.update(kw)
+    return L.rbs_block_stats(a["dt"], a["q"], a["k"], a["S"], a["Hq"], a["Hkv"], a["D"], a["B"],
+                             a["c"], a["r"], a["qr"], a["qn"], None)
+
+
+def test_block_stats_validation(L):
+    assert stats(L, q=None) == E.RBS_E_ARG
+    assert stats(L, k=PM) == E.RBS_E_ARG
+    assert stats(L, c=None) == E.RBS_E_ARG
+    assert stats(L, Hq=6, Hkv=4) == E.RBS_E_ARG
+    assert stats(L, S=-1) == E.RBS_E_ARG
+    assert stats(L, Hkv=0) == E.RBS_E_ARG
+    assert stats(L, dt=7) == E.RBS_E_ARG
+    assert stats(L, D=96) == E.RBS_E_UNSUPPORTED
+    assert stats(L, B=100) == E.RBS_E_UNSUPPORTED
+    assert stats(L, B=512) == E.RBS_E_UNSUPPORTED
+    assert stats(L, S=0) == E.RBS_OK         # empty input: nothing to do, nothing enqueued
+
+
+def select(L, ws=None, wsz=1 << 30, cap=1 << 30, **kw):
+    a = dict(c=P, r=P, qr=P, qn=P, beta=None, Hkv=4, nb=64, D=128, rc=0.1, rr=0.1, flags=0,
+             bo=None, rp=P, ci=P)
+    a.update(kw)
+    size = ctypes.c_size_t(wsz)
+    st = L.rbs_select(a["c"], a["r"], a["qr"], a["qn"], a["beta"], a["Hkv"], a["nb"], a["D"],
+                      a["rc"], a["rr"], a["flags"], a["bo"], a["rp"], a["ci"], cap, ws,
+                      ctypes.byref(size), None)
+    return st, size.value
+
+
+def test_select_workspace_query_and_capacity(L):
+    st, need = select(L, ws=None, wsz=0)
+    assert st == E.RBS_OK and need >= 256 + 4 * 256
+    assert select(L, ws=0x100000, wsz=need - 1)[0] == E.RBS_E_CAPACITY
+    cap = L.rbs_select_capacity(4, 64, 0.1, 0.1, 0)
+    assert cap == orc.select_capacity(4, 64, 0.1, 0.1, False)
+    assert select(L, ws=0x100000, wsz=need, cap=cap - 1)[0] == E.RBS_E_CAPACITY
+    assert L.rbs_select_capacity(4, 1024, 0.03, 0.03, 1) == orc.select_capacity(4, 1024, 0.03, 0.03, True)
+    assert L.rbs_select_capacity(1, 16, 0.25, 0.25, 0) == orc.select_capacity(1, 16, 0.25, 0.25, False)
+    assert L.rbs_select_capacity(0, 16, 0.25, 0.25, 0) == -1
+
+
+def test_select_validation(L):
+    assert select(L, rc=0.0)[0] == E.RBS_E_ARG
+    assert select(L, rr=1.5)[0] == E.RBS_E_ARG
+    assert select(L, rc=float("nan"))[0] == E.RBS_E_ARG
+    assert select(L, flags=0x4)[0] == E.RBS_E_ARG
+    assert select(L, Hkv=0)[0] == E.RBS_E_ARG
+    assert select(L, D=80)[0] == E.RBS_E_UNSUPPORTED
+    assert select(L, nb=100000)[0] == E.RBS_E_UNSUPPORTED
+    assert select(L, ws=0x100001)[0] == E.RBS_E_ARG            # workspace not 256-aligned
+    assert select(L, ws=0x100000, rp=None)[0] == E.RBS_E_ARG
+    st = L.rbs_select(P, P, P, P, None, 4, 64, 128, 0.1, 0.1, 0, None, P, P, 0, None, None, None)
+    assert st == E.RBS_E_ARG                                     # no workspace size pointer
+
+
+def attn(L, **kw):
+    a = dict(dt=0, q=P, k=P, v=P, S=1024, Hq=8, Hkv=2, D=128, B=128, rp=P, ci=P, sc=0.0, o=P,
+             lse=None)
+    a.update(kw)
+    return L.blocksparse_attn_fwd(a["dt"], a["q"], a["k"], a["v"], a["S"], a["Hq"], a["Hkv"],
+                                  a["D"], a["B"], a["rp"], a["ci"], a["sc"], a["o"], a["lse"], None)
+
+
+def test_attention_validation(L):
+    assert attn(L, v=None) == E.RBS_E_ARG
+    assert attn(L, o=PM) == E.RBS_E_ARG
+    assert attn(L, Hq=10, Hkv=4) == E.RBS_E_ARG
+    assert attn(L, sc=float("inf")) == E.RBS_E_ARG
+    assert attn(L, D=64, B=64) == E.RBS_E_UNSUPPORTED           # bf16 supports (128, 128)
+    assert attn(L, dt=1, D=96, B=64) == E.RBS_E_UNSUPPORTED
+    assert attn(L, S=0) == E.RBS_OK
+
+
+def bmask(L, seg=(0, 128, 256, 300), rer=(0, 128, 0), **kw):
+    a = dict(dt=0, q=P, k=P, v=P, S=300, Hq=8, Hkv=2, D=128, theta=5e5, qrb=0, sc=0.0, o=P,
+             lse=None)
+    a.update(kw)
+    n = len(seg) - 1
+    ss = (ctypes.c_int32 * len(seg))(*seg)
+    rr = (ctypes.c_int32 * max(1, len(rer)))(*rer)
+    return L.block_mask_attn_fwd(a["dt"], a["q"], a["k"], a["v"], a["S"], a["Hq"], a["Hkv"],
+                                 a["D"], n, ss, rr, a["theta"], a["qrb"], a["sc"], a["o"],
+                                 a["lse"], None)
+
+
+def test_block_mask_validation(L):
+    assert bmask(L, seg=(0, 256, 128, 300)) == E.RBS_E_ARG      # not increasing
+    assert bmask(L, seg=(0, 128, 256, 299)) == E.RBS_E_ARG      # does not end at S
+    assert bmask(L, seg=(1, 128, 256, 300)) == E.RBS_E_ARG      # does not start at 0
+    assert bmask(L, rer=(0, -5, 0)) == E.RBS_E_ARG
+    assert bmask(L, theta=0.0) == E.RBS_E_ARG
+    assert bmask(L, qrb=301) == E.RBS_E_ARG
+    assert bmask(L, seg=(0, 100, 256, 300)) == E.RBS_E_UNSUPPORTED  # start not on a 128 tile
+    assert bmask(L, dt=1) == E.RBS_E_UNSUPPORTED
+    assert bmask(L, D=64) == E.RBS_E_UNSUPPORTED
+    assert bmask(L, qrb=300) == E.RBS_OK                          # no rows requested

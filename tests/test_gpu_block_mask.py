@@ -1,0 +1,66 @@
+"""GPU parity of Block-attention's RAG mask with RoPE re-encoding of cached
+keys (block_mask_attn_fwd) against the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_rbs_amd as rbs
+from block_sparse_long_rbs_amd import device, inputs
+from oracle import rbs_oracle as orc
+
+import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, q_row_begin=0, tokens=None):
+    H.say(f"[case] {w.name} S={w.seqlen} segments={len(w.seg_start) - 1} q_row_begin={q_row_begin}")
+    t = device.upload(w)
+    sentinel = torch.full_like(t["q"], 7.0)
+    out, lse = rbs.block_mask_attn_fwd(t["q"], t["k"], t["v"], w.seg_start.tolist(),
+                                       w.k_rerotate.tolist(), w.rope_theta,
+                                       q_row_begin=q_row_begin, want_lse=True, out=sentinel)
+    out_h = H.to_host(out)
+    if tokens is None:
+        tokens = np.arange(q_row_begin, w.seqlen)
+    o, l = orc.block_mask_attention(w.q, w.k, w.v, w.seg_start, w.k_rerotate, w.rope_theta,
+                                    q_row_begin=q_row_begin, rows=tokens)
+    d = np.abs(out_h[tokens] - o[tokens])
+    H.say(f"  max-abs {d.max():.3e} mean-abs {d.mean():.3e}")
+    assert d.max() <= H.TOL_BF16_MAX and d.mean() <= H.TOL_BF16_MEAN
+    dl = np.abs(lse.cpu().numpy()[:, tokens] - l[:, tokens]).max()
+    assert dl <= 2e-2, f"lse err {dl}"
+    if q_row_begin > 0:
+        assert np.all(out_h[:q_row_begin] == 7.0), "rows before q_row_begin were written"
+    return out_h
+
+
+def test_rag_small_all_rows_ragged_final_block():
+    w = inputs.rag_layout(n_passages=4, passage_len=256, final_len=200, Hq=8, Hkv=2, seed=31,
+                          name="rag_small")
+    _run(w)
+
+
+def test_rag_small_final_block_only():
+    w = inputs.rag_layout(n_passages=3, passage_len=384, final_len=128, Hq=8, Hkv=4, seed=32,
+                          name="rag_small_final")
+    _run(w, q_row_begin=int(w.seg_start[-2]))
+
+
+def test_rag_zero_offsets_is_plain_segment_attention():
+    """With every re-rotation offset 0 the keys are used as given."""
+    w = inputs.rag_layout(n_passages=2, passage_len=128, final_len=128, Hq=4, Hkv=1, seed=33,
+                          name="rag_zero_off")
+    w.k_rerotate = np.zeros_like(w.k_rerotate)
+    _run(w)
+
+
+def test_rag_31k_sampled_rows():
+    """The 20 x 1,536 + 512 RAG layout, 32/8 heads, theta 5e5: sampled
+    passage rows and final-block rows."""
+    w = inputs.rag_bf16_31k()
+    rng = np.random.default_rng(0)
+    passage_tok = rng.choice(int(w.seg_start[-2]), size=96, replace=False)
+    final_tok = rng.choice(np.arange(int(w.seg_start[-2]), w.seqlen), size=48, replace=False)
+    toks = np.sort(np.concatenate([passage_tok, final_tok, [0, w.seqlen - 1]]))
+    _run(w, tokens=toks)

@@ -1,0 +1,109 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle on
+the same seeded inputs.
+
+Selection: sets bit-exact except blocks whose oracle score lies in the
+threshold band. Attention: run on the oracle's own CSR (so no oracle input
+comes from the GPU) within 2e-2 max-abs / 1e-2 mean-abs for bf16 inputs and
+1e-5 for fp32; end to end (GPU stats -> GPU select -> GPU attention) on rows
+whose GPU block set equals the oracle's.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_rbs_amd as rbs
+from block_sparse_long_rbs_amd import device, inputs
+from oracle import rbs_oracle as orc
+
+import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_f32_1k():
+    """1,024 tokens, GQA 2:1, dim 64, block 64, fp32 (needle blocks, beta = 1)."""
+    H.pipeline_case(inputs.tiny_f32_1k())
+
+
+def test_needle_bf16_8k():
+    H.pipeline_case(inputs.needle_bf16_8k(), sample_rows=24)
+
+
+def test_mixture_bf16_ragged_small():
+    """12 blocks with a 92-token last block; sink on; several tiles per row."""
+    H.pipeline_case(inputs.mixture_small(S=1500, Hq=8, Hkv=2, rho=0.25, sink=True, seed=11))
+
+
+def test_random_f32_ragged_d128():
+    w = inputs.random_qkv(700, 4, 2, 128, "f32", seed=21, block=64, name="random_f32_700",
+                          keep_ratio_centroid=0.3, keep_ratio_rescue=0.2)
+    H.pipeline_case(w)
+
+
+def test_random_f32_block128():
+    w = inputs.random_qkv(1000, 6, 3, 64, "f32", seed=22, block=128, name="random_f32_1000",
+                          keep_ratio_centroid=0.5, keep_ratio_rescue=0.4, sink=True)
+    H.pipeline_case(w)
+
+
+def test_keep_ratio_one_is_dense_bf16():
+    w = inputs.random_qkv(640, 8, 1, 128, "bf16", seed=5, block=128, name="dense_bf16_640",
+                          keep_ratio_centroid=1.0, keep_ratio_rescue=1.0)
+    r = H.pipeline_case(w)
+    rp_h = r["rp"].cpu().numpy()
+    assert rp_h[-1] == 5 * 6 // 2
+
+
+def test_single_partial_block_and_tiny_sequences():
+    for S in (1, 37, 128):
+        w = inputs.random_qkv(S, 2, 1, 128, "bf16", seed=S, block=128, name=f"short_{S}",
+                              keep_ratio_centroid=0.5, keep_ratio_rescue=0.5)
+        H.pipeline_case(w)
+
+
+def test_empty_sequence_is_a_noop():
+    q = torch.zeros((0, 4, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    cen, rad, qr, qn = rbs.rbs_block_stats(q, k, 128)
+    assert cen.shape == (2, 0, 128)
+    rp, ci, _ = rbs.rbs_select(cen, rad, qr, qn, 0.1, 0.1)
+    assert rp.cpu().tolist() == [0]
+    out, _ = rbs.blocksparse_attn_fwd(q, k, k, 128, rp, ci)
+    assert out.shape == q.shape
+
+
+def test_determinism_and_row_permutation():
+    w = inputs.mixture_small(S=1024, Hq=8, Hkv=2, rho=0.3, sink=False, seed=3)
+    t = device.upload(w)
+    res = []
+    for _ in range(2):
+        st = rbs.rbs_block_stats(t["q"], t["k"], w.block)
+        rp, ci, _ = rbs.rbs_select(*st, w.keep_ratio_centroid, w.keep_ratio_rescue)
+        out, lse = rbs.blocksparse_attn_fwd(t["q"], t["k"], t["v"], w.block, rp, ci, want_lse=True)
+        res.append((rp.cpu(), ci.cpu(), out.cpu(), lse.cpu()))
+    for a, b in zip(res[0], res[1]):
+        assert torch.equal(a, b)
+    # reversing every CSR row changes the accumulation order, not the result
+    rp_h = res[0][0].numpy()
+    ci_h = res[0][1].numpy()[:rp_h[-1]].copy()
+    for r in range(len(rp_h) - 1):
+        ci_h[rp_h[r]:rp_h[r + 1]] = ci_h[rp_h[r]:rp_h[r + 1]][::-1]
+    rp_d, ci_d = H.csr_to_device(rp_h, ci_h)
+    out2, _ = rbs.blocksparse_attn_fwd(t["q"], t["k"], t["v"], w.block, rp_d, ci_d)
+    d = (out2.float() - res[0][2].cuda().float()).abs()
+    assert d.max().item() <= 2e-2 and d.mean().item() <= 1e-3
+
+
+def test_csr_entries_outside_the_causal_range_are_skipped():
+    w = inputs.random_qkv(512, 4, 1, 128, "bf16", seed=8, block=128, name="skip")
+    t = device.upload(w)
+    rp, ci = orc.dense_causal_selection(1, 4)
+    # add out-of-range entries (> i and negative) to every row
+    rows = [list(ci[rp[i]:rp[i + 1]]) + [i + 1, -3, 99] for i in range(4)]
+    rp2 = np.zeros(5, np.int64)
+    np.cumsum([len(r) for r in rows], out=rp2[1:])
+    a, b = H.csr_to_device(rp2, np.concatenate(rows))
+    out, _ = rbs.blocksparse_attn_fwd(t["q"], t["k"], t["v"], 128, a, b)
+    o, _ = orc.blocksparse_attention(w.q, w.k, w.v, 128, rp, ci)
+    d = np.abs(H.to_host(out) - o)
+    assert d.max() <= H.TOL_BF16_MAX and d.mean() <= H.TOL_BF16_MEAN
