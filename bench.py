@@ -1,0 +1,271 @@
+"""Benchmark of one RBS prefill-attention layer on one MI355X.
+
+A step is one pass of the hot path over the 128K workload: block statistics
+(rbs_block_stats), dual-branch selection into CSR lists (rbs_select) and
+block-sparse attention over the selected blocks (blocksparse_attn_fwd), all
+on torch's current stream with inputs already resident in HBM.
+
+Prints one JSON line. `value` is effective TFLOP/s of the whole step: the
+attention flops on the selected blocks (4*D per admitted (query, key) pair,
+counted from the emitted CSR) divided by the step time. `ms_per_step` is
+ms/layer. `roofline` covers the dominant kernel (attention) against the
+bf16 matrix-core peak; `phases` holds per-kernel HIP-event times and the
+stats+select HBM fraction; `cpu_baseline` times the float64 CPU oracle on a
+bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--no-extras]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 matrix-core peak (256 CU x 2.4 GHz x 4096 flop/clk)
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+METRIC = "block-sparse prefill attn ms/layer + effective TFLOP/s (% bf16 peak) at 128K"
+
+
+def selected_pairs(row_ptr: np.ndarray, col_idx: np.ndarray, S: int, B: int, Hkv: int) -> int:
+    """(query token, key token) pairs one query head admits, summed over KV
+    groups: full blocks below the diagonal, the causal triangle on it."""
+    nb = -(-S // B)
+    rows = np.repeat(np.arange(Hkv * nb), np.diff(row_ptr))
+    i = rows % nb
+    j = col_idx.astype(np.int64)
+    qlen = np.minimum(S, (i + 1) * B) - i * B
+    klen = np.minimum(S, (j + 1) * B) - j * B
+    full = np.where(j < i, qlen * klen, 0)
+    diag = np.where(j == i, qlen * (qlen + 1) // 2, 0)
+    return int(full.sum() + diag.sum())
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the dense ratio and the Block-attention workload")
+    ap.add_argument("--cpu-rows", type=int, default=16)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one 1 GiB device-to-device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has "
+              "no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_long_rbs_amd as rbs
+    from block_sparse_long_rbs_amd import device, inputs
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    torch.cuda.set_device(0)
+    t_gen = time.perf_counter()
+    w = inputs.mixture_bf16_128k()
+    log(f"generated {w.name} in {time.perf_counter() - t_gen:.1f}s")
+    t = device.upload(w)
+    S, Hq, Hkv, D, B = w.seqlen, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block
+    G = Hq // Hkv
+    nb = w.n_blocks
+    cap = rbs.rbs_select_capacity(Hkv, nb, w.keep_ratio_centroid, w.keep_ratio_rescue, w.sink)
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(t["q"])
+
+    def step():
+        cen, rad, qr, qn = rbs.rbs_block_stats(t["q"], t["k"], B)
+        rp, ci, _ = rbs.rbs_select(cen, rad, qr, qn, w.keep_ratio_centroid, w.keep_ratio_rescue,
+                                   sink=w.sink, workspace=ws)
+        rbs.blocksparse_attn_fwd(t["q"], t["k"], t["v"], B, rp, ci, out=out)
+        return rp, ci
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        ev[s][0].record(stream)
+        cen, rad, qr, qn = rbs.rbs_block_stats(t["q"], t["k"], B)
+        ev[s][1].record(stream)
+        rp, ci, _ = rbs.rbs_select(cen, rad, qr, qn, w.keep_ratio_centroid, w.keep_ratio_rescue,
+                                   sink=w.sink, workspace=ws)
+        ev[s][2].record(stream)
+        rbs.blocksparse_attn_fwd(t["q"], t["k"], t["v"], B, rp, ci, out=out)
+        ev[s][3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / K
+    t_stats = float(np.mean([ev[s][0].elapsed_time(ev[s][1]) for s in range(K)]))
+    t_sel = float(np.mean([ev[s][1].elapsed_time(ev[s][2]) for s in range(K)]))
+    t_attn = float(np.mean([ev[s][2].elapsed_time(ev[s][3]) for s in range(K)]))
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    ci_h = ci[:int(rp_h[-1])].cpu().numpy()
+    pairs = selected_pairs(rp_h, ci_h, S, B, Hkv) * G
+    flops = 4.0 * D * pairs
+    attn_tflops = flops / (t_attn * 1e-3) / 1e12
+    value = flops / (ms_step * 1e-3) / 1e12
+    stats_bytes = S * (Hq + Hkv) * D * 2 + 2 * Hkv * nb * (D + 1) * 4
+    select_bytes = 2 * Hkv * nb * (D + 1) * 4 + (Hkv * nb + 1) * 4 + int(rp_h[-1]) * 4
+    log(f"step {ms_step:.3f} ms: stats {t_stats:.3f} select {t_sel:.3f} attn {t_attn:.3f} ms; "
+        f"attention {attn_tflops:.1f} TFLOP/s")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "seqlen": S, "n_q_heads": Hq, "n_kv_heads": Hkv,
+                   "head_dim": D, "block": B, "keep_ratio_per_branch": w.keep_ratio_centroid,
+                   "sink": w.sink, "beta": "derived", "seed": w.seed},
+        "roofline": {"bound": "mfma", "kernel": "attn_csr_bf16_kernel",
+                     "achieved": round(attn_tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "phases": {
+            "stats_ms": round(t_stats, 4), "select_ms": round(t_sel, 4),
+            "attn_ms": round(t_attn, 4),
+            "attn_flops": flops, "selected_pairs_per_head": pairs // G,
+            "csr_nnz": int(rp_h[-1]),
+            "stats_gbs": round(stats_bytes / (t_stats * 1e-3) / 1e9, 1),
+            "stats_hbm_frac": round(stats_bytes / (t_stats * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "stats_select_hbm_frac": round((stats_bytes + select_bytes) /
+                                           ((t_stats + t_sel) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "stats_bytes": stats_bytes, "select_bytes": select_bytes,
+        },
+    }
+
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    if not args.no_extras:
+        # dense causal attention through the same kernel (keep-ratio 1) for the sparse/dense ratio
+        rows = [np.arange(i + 1, dtype=np.int32) for _ in range(Hkv) for i in range(nb)]
+        rpd = np.zeros(Hkv * nb + 1, np.int64)
+        np.cumsum([len(r) for r in rows], out=rpd[1:])
+        rpd_t = torch.from_numpy(rpd.astype(np.int32)).cuda()
+        cid_t = torch.from_numpy(np.concatenate(rows)).cuda()
+        rbs.blocksparse_attn_fwd(t["q"], t["k"], t["v"], B, rpd_t, cid_t, out=out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(2):
+            rbs.blocksparse_attn_fwd(t["q"], t["k"], t["v"], B, rpd_t, cid_t, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_dense = e0.elapsed_time(e1) / 2
+        dense_flops = 4.0 * D * Hq * (S * (S + 1) // 2)
+        result["dense_reference"] = {
+            "attn_ms": round(t_dense, 3),
+            "tflops": round(dense_flops / (t_dense * 1e-3) / 1e12, 1),
+            "sparse_over_dense_speedup": round(t_dense / t_attn, 2),
+        }
+        log(f"dense causal attention {t_dense:.2f} ms -> speedup {t_dense / t_attn:.2f}x")
+        del rpd_t, cid_t
+        # Block-attention RAG workload
+        wr = inputs.rag_bf16_31k()
+        tr = device.upload(wr)
+        outr = torch.empty_like(tr["q"])
+        args_r = (tr["q"], tr["k"], tr["v"], wr.seg_start.tolist(), wr.k_rerotate.tolist(),
+                  wr.rope_theta)
+        for _ in range(3):
+            rbs.block_mask_attn_fwd(*args_r, out=outr)
+        e0.record(stream)
+        for _ in range(10):
+            rbs.block_mask_attn_fwd(*args_r, out=outr)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_bm = e0.elapsed_time(e1) / 10
+        seg = wr.seg_start
+        pairs_bm = 0
+        for p in range(len(seg) - 1):
+            L = int(seg[p + 1] - seg[p])
+            lo = 0 if p == len(seg) - 2 else int(seg[p])
+            pairs_bm += L * (int(seg[p]) - lo) + L * (L + 1) // 2
+        fl_bm = 4.0 * wr.head_dim * wr.n_q_heads * pairs_bm
+        result["block_mask_rag_31k"] = {"attn_ms": round(t_bm, 4),
+                                        "tflops": round(fl_bm / (t_bm * 1e-3) / 1e12, 1),
+                                        "flops": fl_bm}
+        log(f"block-mask RAG 31K: {t_bm:.3f} ms, {fl_bm / (t_bm * 1e-3) / 1e12:.1f} TFLOP/s")
+        del tr, outr
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, flops, args.cpu_rows, log)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, flops_total, n_rows, log):
+    """The float64 oracle on the host cores: stats and selection over the full
+    workload, attention on n_rows sampled (KV head, query block) rows,
+    extrapolated to the whole layer by their share of the attention flops."""
+    from oracle import rbs_oracle as orc
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    c, r, qr, qn = orc.block_stats(w.q, w.k, w.n_kv_heads, w.block)
+    t_stats = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    sel = orc.select(c, r, qr, qn, orc.derive_beta(r), w.keep_ratio_centroid,
+                     w.keep_ratio_rescue, w.sink)
+    t_sel = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    nb = w.n_blocks
+    all_rows = [(g, i) for g in range(w.n_kv_heads) for i in range(nb)]
+    rows = [all_rows[k] for k in rng.choice(len(all_rows), size=n_rows, replace=False)]
+    t0 = time.perf_counter()
+    orc.blocksparse_attention(w.q, w.k, w.v, w.block, sel.row_ptr, sel.col_idx, rows=rows)
+    t_attn_sample = time.perf_counter() - t0
+    sub_ptr = [0]
+    sub_idx = []
+    for g, i in rows:
+        rr = g * nb + i
+        blk = sel.col_idx[sel.row_ptr[rr]:sel.row_ptr[rr + 1]]
+        sub_idx.extend(blk.tolist())
+        sub_ptr.append(len(sub_idx))
+    # flops of the sampled rows
+    fl = 0
+    for (g, i), a, b in zip(rows, sub_ptr[:-1], sub_ptr[1:]):
+        for j in sub_idx[a:b]:
+            L = min(w.seqlen, (i + 1) * w.block) - i * w.block
+            fl += (L * L if j < i else L * (L + 1) // 2)
+    fl *= 4.0 * w.head_dim * w.group
+    t_attn_full = t_attn_sample * flops_total / max(fl, 1.0)
+    t_total = t_stats + t_sel + t_attn_full
+    val = flops_total / t_total / 1e12
+    log(f"cpu oracle: stats {t_stats:.1f}s select {t_sel:.1f}s attention sample {t_attn_sample:.1f}s "
+        f"-> {t_total:.0f}s per layer ({val:.4f} TFLOP/s)")
+    return {"value": round(val, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": (f"float64 NumPy oracle on the same 128K inputs: block stats and selection "
+                       f"over all {w.n_kv_heads * nb} rows ({t_stats:.1f}s + {t_sel:.1f}s), "
+                       f"attention on {n_rows} random (KV head, query block) rows "
+                       f"({t_attn_sample:.1f}s for {fl:.3g} flops), extrapolated by flops to "
+                       f"the whole layer: {t_total:.0f}s per layer"),
+            "seconds_per_layer": round(t_total, 1)}
+
+
+if __name__ == "__main__":
+    main()

@@ -284,6 +284,258 @@ __global__ __launch_bounds__(kThreads, 2) void attn_csr_bf16_kernel(AttnArgs a, 
   store_out(static_cast<uint16_t*>(a.out), a.lse, a.S, a.Hq, u.h, u.qt, 0, o, sm);
 }
 
+// ---------------------------------------------------------------------------
+// CSR core, version 2: K and V tiles go straight from global memory into
+// swizzled LDS with global_load_lds_dwordx4 (no staging registers), V^T
+// fragments are read with the transposing LDS load ds_read_b64_tr_b16, and the
+// K and V buffers are refilled separately: the next tile's K streams in
+// during this tile's softmax and P.V, the next V during the next Q.K^T.
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
+// 16-byte chunk swizzles: K rows are read 16 rows x one chunk per MFMA
+// fragment, V rows 4 rows x four chunks per transposing read.
+__device__ __forceinline__ int k_swz(int row) { return row & 15; }
+__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
+
+// Workgroup barrier for LDS hand-offs: this wave's LDS reads/writes are
+// complete, then s_barrier. No memory fence, so tile DMAs (vector-memory
+// writes into LDS) stay in flight across it; their completion is awaited
+// explicitly with wait_vmcnt before the barrier that publishes them.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// DMA one 128 x 128 bf16 tile (tokens key0.., one KV head; src already points
+// at that head) into LDS. Each of the 4 waves issues 8 loads of 1 KB (4 rows);
+// lane l of a load lands at base + 16 l, so each lane fetches the logical
+// chunk that the swizzle puts there. Rows past the sequence end repeat the
+// last row (finite values; their scores are masked).
+// One 16-byte-per-lane DMA from global memory into LDS at lds_addr + 16*lane.
+// Issued as inline asm so that the compiler does not treat it as a pending
+// LDS write (it would otherwise wait for every in-flight tile before each LDS
+// read); completion is awaited explicitly with wait_vmcnt.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+template <bool IS_V>
+__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, size_t rs, int S,
+                                         int key0, char* lds) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r4 = lane >> 4, pc = lane & 15;
+  const uint32_t dst = lds_u32(lds) + wave * 8 * 1024;
+  const int row0 = key0 + wave * 32;
+  if (row0 + 32 <= S) {
+    // whole 32-row slice present: scalar row base + per-lane offset
+    const uint16_t* base = src + (size_t)row0 * rs;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int lc = IS_V ? (pc ^ (r4 << 2)) : (pc ^ (((it & 3) << 2) | r4));
+      dma16(base + (size_t)(it * 4) * rs + (r4 * rs + lc * 8), dst + it * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int lc = IS_V ? (pc ^ (r4 << 2)) : (pc ^ (((it & 3) << 2) | r4));
+      const int tok = min(row0 + it * 4 + r4, S - 1);
+      dma16(src + (size_t)tok * rs + lc * 8, dst + it * 1024);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void attn_csr_bf16_v2_kernel(
+    AttnArgs a, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+    float scale_log2) {
+  __shared__ __attribute__((aligned(1024))) char Ks[TILE * ROWB];
+  __shared__ __attribute__((aligned(1024))) char Vs[TILE * ROWB];
+  const int G = a.Hq / a.Hkv;
+  const int nq = (a.S + TILE - 1) / TILE;
+  Unit u;
+  if (!decode_unit(G, a.Hkv, nq, 0, u)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m32 = lane & 31, hh = lane >> 5;
+  const size_t rs = (size_t)a.Hkv * D;
+  const uint16_t* Kg = static_cast<const uint16_t*>(a.k) + (size_t)u.g * D;
+  const uint16_t* Vg = static_cast<const uint16_t*>(a.v) + (size_t)u.g * D;
+
+  // CSR row, staged through LDS 256 entries at a time (a vector load inside the
+  // tile loop would make every wait drain the in-flight tile DMAs)
+  __shared__ int lst[kThreads];
+  const int row = u.g * nq + u.qt;
+  const int e0 = row_ptr[row], e1 = row_ptr[row + 1];
+  int cb = e0;
+  lst[threadIdx.x] = (e0 + (int)threadIdx.x < e1) ? col_idx[e0 + threadIdx.x] : -1;
+  lds_barrier();
+  auto next_valid = [&](int e, int& j) {
+    for (; e < e1; ++e) {
+      if (e - cb >= kThreads) {  // refill: every wave reaches this point together
+        lds_barrier();
+        cb = e;
+        lst[threadIdx.x] = (cb + (int)threadIdx.x < e1) ? col_idx[cb + threadIdx.x] : -1;
+        lds_barrier();
+      }
+      j = lst[e - cb];
+      if (j >= 0 && j <= u.qt) return e;
+    }
+    j = -1;
+    return e1;
+  };
+
+  bf16x8_t qf[8];
+  load_q(static_cast<const uint16_t*>(a.q), a.S, a.Hq, u.h, u.qt, qf);
+  f32x16_t o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = (f32x16_t){};
+  float m_run = -1e30f, l_run = 0.f;
+
+  // per-lane LDS offsets
+  const int kx = m32 & 15;
+  const int sr = lane & 15, half = (lane >> 4) & 1, y = sr >> 2;
+  const int v_lane = (4 * hh + y) * ROWB + (sr & 1) * 8;
+  const int vx = 2 * half + ((sr & 3) >> 1);
+  const int qq = wave * 32 + m32;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  int j;
+  int e = next_valid(e0, j);
+  wait_vmcnt<0>();  // Q fragments and the CSR chunk are in registers before any tile DMA
+  if (e < e1) {
+    dma_tile<false>(Kg, rs, a.S, j * TILE, Ks);
+    dma_tile<true>(Vg, rs, a.S, j * TILE, Vs);
+  }
+  while (e < e1) {
+    int jn;
+    const int en = next_valid(e + 1, jn);
+    wait_vmcnt<8>();  // K(j) has landed (V(j) may still be in flight)
+    lds_barrier();
+    // ---- S^T = K Q^T ----
+    f32x16_t s[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const char* rowp = Ks + (kb * 32 + m32) * ROWB;
+      s[kb] = (f32x16_t){};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint4 af = *reinterpret_cast<const uint4*>(rowp + (((2 * c + hh) ^ kx) << 4));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af), qf[c], s[kb], 0, 0, 0);
+      }
+    }
+    // keep up to 8 fragment reads in flight ahead of the matrix instructions
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 24; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    lds_barrier();  // every wave is done with Ks
+    if (jn >= 0) dma_tile<false>(Kg, rs, a.S, jn * TILE, Ks);
+    // ---- online softmax (base 2), lazy rescale by at most 2^8 ----
+    if (j == u.qt) {
+      // causal mask inside the diagonal tile; t is made opaque so that the
+      // per-element predicates are not hoisted out of the tile loop
+      int t = qq - 4 * hh;
+      asm volatile("" : "+v"(t));
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + (r & 3) > t) s[kb][r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mt = mx * scale_log2;
+    const bool grow = mt > m_run + 8.f;
+    if (__ballot(grow)) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
+      m_run = grow ? mt : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+    const float neg = -m_run;
+    uint32_t pk[4][8];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, neg));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], scale_log2, neg));
+        const uint32_t w = cvt_pk_bf16(p0, p1);
+        pk[kb][r >> 1] = w;
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, l_run,
+                                                false);
+      }
+    if (jn >= 0) wait_vmcnt<8>(); else wait_vmcnt<0>();  // V(j) has landed
+    lds_barrier();
+    // ---- O^T += V^T P^T ----
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const char* vb = Vs + v_lane + ((((db ^ y) << 2) + vx) << 4);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)(vb + c * 16 * ROWB));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)(vb + c * 16 * ROWB + 8 * ROWB));
+        const uint4 av = make_uint4(
+            (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+            (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+            (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+            (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16));
+        const int kb = c >> 1, base = (c & 1) * 4;
+        const uint4 b = make_uint4(pk[kb][base], pk[kb][base + 1], pk[kb][base + 2],
+                                   pk[kb][base + 3]);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(b), o[db], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 28; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    lds_barrier();  // every wave is done with Vs
+    if (jn >= 0) dma_tile<true>(Vg, rs, a.S, jn * TILE, Vs);
+    e = en;
+    j = jn;
+  }
+  Softmax sm{m_run, l_run};
+  store_out(static_cast<uint16_t*>(a.out), a.lse, a.S, a.Hq, u.h, u.qt, 0, o, sm);
+}
+
 __device__ __forceinline__ int segment_of_tile(const SegArgs& s, int tile) {
   const int tok = tile * TILE;
   int lo = 0, hi = s.n_seg - 1;  // last p with start[p] <= tok
@@ -348,8 +600,8 @@ inline int attn_grid(int Hq, int Hkv, int n_qt) {
 rbs_status launch_attn_bf16_csr(const AttnArgs& a, hipStream_t st) {
   const float scale_log2 = a.scale * 1.4426950408889634f;
   const int nq = (a.S + TILE - 1) / TILE;
-  hipLaunchKernelGGL(attn_csr_bf16_kernel, dim3(attn_grid(a.Hq, a.Hkv, nq)), dim3(kThreads), 0, st,
-                     a, scale_log2);
+  hipLaunchKernelGGL(attn_csr_bf16_v2_kernel, dim3(attn_grid(a.Hq, a.Hkv, nq)), dim3(kThreads), 0,
+                     st, a, a.row_ptr, a.col_idx, scale_log2);
   return launch_status();
 }
 
