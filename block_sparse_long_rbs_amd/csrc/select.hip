@@ -25,7 +25,6 @@ namespace rbs {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxRows = 16;          // query blocks per workgroup
 constexpr size_t kLdsBudget = 64 * 1024;  // bytes of LDS per workgroup
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -46,11 +45,178 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// n-th largest key among lane-strided candidates j < nvis (keys from LDS via
-// the functor), then the membership of j by (key > T) or (key == T and among
-// the first `need` ties by ascending j).
+// Radix select over order-preserving 32-bit keys: the n-th largest key
+// among the row's candidates (lane-strided, M per lane; absent candidates
+// carry key 0, below every real key). Bits are fixed from the top; it stops
+// as soon as exactly n keys are >= the prefix, which then is a valid
+// threshold (every key above it is kept, none below).
+template <int M>
+__device__ __forceinline__ uint32_t nth_largest_regs(const uint32_t (&key)[M], int n) {
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int m = 0; m < M; ++m) cnt += __popcll(__ballot(key[m] >= cand));
+    if (cnt >= n) {
+      T = cand;
+      if (cnt == n) break;
+    }
+  }
+  return T;
+}
+
+// Keep the keys > T plus the first (n - #keys > T) keys equal to T in
+// ascending index order; returns this lane's membership bits.
+template <int M>
+__device__ __forceinline__ uint32_t take_top(const uint32_t (&key)[M], int n, uint32_t T) {
+  int gt = 0;
+#pragma unroll
+  for (int m = 0; m < M; ++m) gt += __popcll(__ballot(key[m] > T));
+  int need = n - gt;
+  uint32_t bits = 0;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const uint64_t tie = __ballot(key[m] == T);
+    const int rank = __popcll(tie & lanemask_lt());
+    if (key[m] > T || (key[m] == T && rank < need)) bits |= 1u << m;
+    need -= __popcll(tie);
+  }
+  return bits;
+}
+
+constexpr int kSelRows = 8;   // query blocks per workgroup
+constexpr int kSelM = 16;     // candidates per lane held in registers (nb <= 1024)
+
+// Scores for kSelRows query blocks x (i0 + kSelRows) key blocks, then one wave
+// per query block selects.
+template <int M>
+__global__ __launch_bounds__(kThreads) void select_v2_kernel(SelectArgs a, int R) {
+  extern __shared__ float smem[];
+  const int g = blockIdx.y;
+  const int nb = a.nb, D = a.D;
+  // heaviest row groups first
+  const int grp = gridDim.x - 1 - blockIdx.x;
+  const int i0 = grp * R;
+  const int rows = min(R, nb - i0);
+  const int ncols = i0 + rows;
+  const int pitch = (ncols + 3) & ~3;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+
+  float* rb = smem;                  // [nb] r_j * beta_j
+  float* qrow = rb + ((nb + 3) & ~3);  // [R][D]
+  float* red = qrow + R * D;         // [16]
+  float* sc = red + 16;              // [R][pitch]
+
+  const float* rad = a.rad + (size_t)g * nb;
+  if (a.beta_in) {
+    const float* bi = a.beta_in + (size_t)g * nb;
+    for (int j = tid; j < ncols; j += kThreads) rb[j] = rad[j] * bi[j];
+    if (a.beta_out && grp == 0)
+      for (int j = tid; j < nb; j += kThreads) a.beta_out[(size_t)g * nb + j] = bi[j];
+  } else {
+    float sum = 0.f, mx = 0.f;
+    for (int j = tid; j < nb; j += kThreads) {
+      const float r = rad[j];
+      sum += r;
+      mx = fmaxf(mx, r);
+    }
+    sum = wave_sum(sum);
+    mx = wave_max(mx);
+    if (lane == 0) { red[wave] = sum; red[4 + wave] = mx; }
+    __syncthreads();
+    const float mean = (red[0] + red[1] + red[2] + red[3]) / (float)nb;
+    const float top = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
+    const float spread = top - mean;
+    const bool ok = spread > 1e-6f * top;
+    const int jend = (a.beta_out && grp == 0) ? nb : ncols;
+    for (int j = tid; j < jend; j += kThreads) {
+      const float b = ok ? fminf(fmaxf((rad[j] - mean) / spread, 0.f), 1.f) : 0.f;
+      if (j < ncols) rb[j] = rad[j] * b;
+      if (a.beta_out && grp == 0) a.beta_out[(size_t)g * nb + j] = b;
+    }
+  }
+  for (int x = tid; x < rows * D; x += kThreads) qrow[x] = a.qrep[((size_t)g * nb + i0) * D + x];
+  __syncthreads();
+
+  // ---- centroid scores: each thread a (R rows x 4 columns) register tile ----
+  const float* cen = a.cen + (size_t)g * nb * D;
+  for (int j0 = 4 * tid; j0 < ncols; j0 += 4 * kThreads) {
+    float acc[kSelRows][4];
+#pragma unroll
+    for (int r = 0; r < kSelRows; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+    const float4* cj[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      cj[c] = reinterpret_cast<const float4*>(cen + (size_t)min(j0 + c, ncols - 1) * D);
+    for (int d4 = 0; d4 < D / 4; ++d4) {
+      float4 cv[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) cv[c] = cj[c][d4];
+#pragma unroll
+      for (int r = 0; r < kSelRows; ++r) {
+        if (r < rows) {
+          const float4 qv = reinterpret_cast<const float4*>(qrow + r * D)[d4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            acc[r][c] = fmaf(qv.x, cv[c].x, acc[r][c]);
+            acc[r][c] = fmaf(qv.y, cv[c].y, acc[r][c]);
+            acc[r][c] = fmaf(qv.z, cv[c].z, acc[r][c]);
+            acc[r][c] = fmaf(qv.w, cv[c].w, acc[r][c]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kSelRows; ++r)
+      if (r < rows)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (j0 + c < ncols) sc[r * pitch + j0 + c] = acc[r][c];
+  }
+  __syncthreads();
+
+  // ---- per-row selection, one wave per query block ----
+  for (int r = wave; r < rows; r += kThreads / 64) {
+    const int i = i0 + r;
+    const int nvis = i + 1;
+    const float qn = a.qnorm[(size_t)g * nb + i];
+    const float* srow = sc + r * pitch;
+    uint32_t kc[M], kr[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int j = lane + 64 * m;
+      const bool in = j < nvis;
+      const float sv = in ? srow[j] : 0.f;
+      kc[m] = in ? order_key(sv) : 0u;
+      kr[m] = in ? order_key(fmaf(qn, rb[j], sv)) : 0u;
+    }
+    const int nc = budget(nvis, a.rho_c);
+    const int nr = budget(nvis, a.rho_r);
+    const uint32_t bc = take_top(kc, nc, nth_largest_regs(kc, nc));
+    const uint32_t br = take_top(kr, nr, nth_largest_regs(kr, nr));
+    int base = 0;
+    int32_t* out = a.lists + ((size_t)g * nb + i) * a.stride;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int j = lane + 64 * m;
+      const bool sel = j < nvis && ((((bc | br) >> m) & 1u) || j == i || (a.sink && j == 0));
+      const uint64_t msk = __ballot(sel);
+      const int pos = base + __popcll(msk & lanemask_lt());
+      if (sel && pos < a.stride) out[pos] = j;
+      base += __popcll(msk);
+    }
+    if (lane == 0) a.counts[(size_t)g * nb + i] = min(base, a.stride);
+  }
+}
+
+// Generic path for long rows (nb > 1024): keys are recomputed from LDS
+// on every pass instead of being held in registers.
 template <typename KeyFn>
-__device__ __forceinline__ uint32_t nth_largest(int nvis, int n, KeyFn key) {
+__device__ uint32_t nth_largest_lds(int nvis, int n, KeyFn key) {
   const int lane = threadIdx.x & 63;
   uint32_t T = 0;
   for (int bit = 31; bit >= 0; --bit) {
@@ -58,102 +224,88 @@ __device__ __forceinline__ uint32_t nth_largest(int nvis, int n, KeyFn key) {
     int cnt = 0;
     for (int j0 = 0; j0 < nvis; j0 += 64) {
       const int j = j0 + lane;
-      const bool p = j < nvis && key(j) >= cand;
-      cnt += __popcll(__ballot(p));
+      cnt += __popcll(__ballot(j < nvis && key(j) >= cand));
     }
-    if (cnt >= n) T = cand;
+    if (cnt >= n) {
+      T = cand;
+      if (cnt == n) break;
+    }
   }
   return T;
 }
 
-__global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a, int R) {
+__global__ __launch_bounds__(kThreads) void select_long_kernel(SelectArgs a, int R) {
   extern __shared__ float smem[];
   const int g = blockIdx.y;
-  const int i0 = blockIdx.x * R;
   const int nb = a.nb, D = a.D;
+  const int grp = gridDim.x - 1 - blockIdx.x;
+  const int i0 = grp * R;
   const int rows = min(R, nb - i0);
-  const int imax = i0 + rows - 1;
-  const int ncols = imax + 1;
+  const int ncols = i0 + rows;
+  const int pitch = (ncols + 3) & ~3;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-
-  float* rb = smem;                         // [nb] r_j * beta_j
-  float* qrow = rb + nb;                    // [R][D]
-  float* red = qrow + R * D;                // [16]
-  float* sc = red + 16;                     // [R][ncols_pad]
-  const int pitch = (ncols + 3) & ~3;
-
+  float* rb = smem;
+  float* qrow = rb + ((nb + 3) & ~3);
+  float* red = qrow + R * D;
+  float* sc = red + 16;
   const float* rad = a.rad + (size_t)g * nb;
-  // ---- rescue coefficient ----
   if (a.beta_in) {
     const float* bi = a.beta_in + (size_t)g * nb;
-    for (int j = tid; j < nb; j += kThreads) rb[j] = rad[j] * bi[j];
-    if (a.beta_out && blockIdx.x == 0)
+    for (int j = tid; j < ncols; j += kThreads) rb[j] = rad[j] * bi[j];
+    if (a.beta_out && grp == 0)
       for (int j = tid; j < nb; j += kThreads) a.beta_out[(size_t)g * nb + j] = bi[j];
   } else {
-    float s = 0.f, m = 0.f;
+    float sum = 0.f, mx = 0.f;
     for (int j = tid; j < nb; j += kThreads) {
-      s += rad[j];
-      m = fmaxf(m, rad[j]);
+      sum += rad[j];
+      mx = fmaxf(mx, rad[j]);
     }
-    s = wave_sum(s);
-    m = wave_max(m);
-    if (lane == 0) { red[wave] = s; red[4 + wave] = m; }
+    sum = wave_sum(sum);
+    mx = wave_max(mx);
+    if (lane == 0) { red[wave] = sum; red[4 + wave] = mx; }
     __syncthreads();
     const float mean = (red[0] + red[1] + red[2] + red[3]) / (float)nb;
-    const float mx = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
-    const float spread = mx - mean;
-    const bool ok = spread > 1e-6f * mx;
-    for (int j = tid; j < nb; j += kThreads) {
-      float b = ok ? fminf(fmaxf((rad[j] - mean) / spread, 0.f), 1.f) : 0.f;
-      rb[j] = rad[j] * b;
-      if (a.beta_out && blockIdx.x == 0) a.beta_out[(size_t)g * nb + j] = b;
+    const float top = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
+    const float spread = top - mean;
+    const bool ok = spread > 1e-6f * top;
+    const int jend = (a.beta_out && grp == 0) ? nb : ncols;
+    for (int j = tid; j < jend; j += kThreads) {
+      const float b = ok ? fminf(fmaxf((rad[j] - mean) / spread, 0.f), 1.f) : 0.f;
+      if (j < ncols) rb[j] = rad[j] * b;
+      if (a.beta_out && grp == 0) a.beta_out[(size_t)g * nb + j] = b;
     }
   }
-  // ---- representative queries of this workgroup's rows ----
-  for (int x = tid; x < rows * D; x += kThreads)
-    qrow[x] = a.qrep[((size_t)g * nb + i0) * D + x];
+  for (int x = tid; x < rows * D; x += kThreads) qrow[x] = a.qrep[((size_t)g * nb + i0) * D + x];
   __syncthreads();
-
-  // ---- centroid scores: one column j per thread, all R rows at once ----
   const float* cen = a.cen + (size_t)g * nb * D;
   for (int j = tid; j < ncols; j += kThreads) {
-    float acc[kMaxRows];
-#pragma unroll
-    for (int r = 0; r < kMaxRows; ++r) acc[r] = 0.f;
     const float4* cj = reinterpret_cast<const float4*>(cen + (size_t)j * D);
-    for (int d4 = 0; d4 < D / 4; ++d4) {
-      const float4 c = cj[d4];
-#pragma unroll
-      for (int r = 0; r < kMaxRows; ++r) {
-        if (r < rows) {
-          const float4 qv = reinterpret_cast<const float4*>(qrow + r * D)[d4];
-          acc[r] = fmaf(qv.x, c.x, acc[r]);
-          acc[r] = fmaf(qv.y, c.y, acc[r]);
-          acc[r] = fmaf(qv.z, c.z, acc[r]);
-          acc[r] = fmaf(qv.w, c.w, acc[r]);
-        }
+    for (int r = 0; r < rows; ++r) {
+      float acc = 0.f;
+      for (int d4 = 0; d4 < D / 4; ++d4) {
+        const float4 c = cj[d4];
+        const float4 qv = reinterpret_cast<const float4*>(qrow + r * D)[d4];
+        acc = fmaf(qv.x, c.x, acc);
+        acc = fmaf(qv.y, c.y, acc);
+        acc = fmaf(qv.z, c.z, acc);
+        acc = fmaf(qv.w, c.w, acc);
       }
+      sc[r * pitch + j] = acc;
     }
-#pragma unroll
-    for (int r = 0; r < kMaxRows; ++r)
-      if (r < rows) sc[r * pitch + j] = acc[r];
   }
   __syncthreads();
-
-  // ---- per-row selection, one wave per row ----
   for (int r = wave; r < rows; r += kThreads / 64) {
     const int i = i0 + r;
     const int nvis = i + 1;
     const float qn = a.qnorm[(size_t)g * nb + i];
-    const float* s = sc + r * pitch;
-    auto keyc = [&](int j) { return order_key(s[j]); };
-    auto keyr = [&](int j) { return order_key(fmaf(qn, rb[j], s[j])); };
+    const float* srow = sc + r * pitch;
+    auto keyc = [&](int j) { return order_key(srow[j]); };
+    auto keyr = [&](int j) { return order_key(fmaf(qn, rb[j], srow[j])); };
     const int nc = budget(nvis, a.rho_c);
     const int nr = budget(nvis, a.rho_r);
-    const uint32_t Tc = nth_largest(nvis, nc, keyc);
-    const uint32_t Tr = nth_largest(nvis, nr, keyr);
-    // ties at the threshold: how many are needed, by ascending j
+    const uint32_t Tc = nth_largest_lds(nvis, nc, keyc);
+    const uint32_t Tr = nth_largest_lds(nvis, nr, keyr);
     int gtc = 0, gtr = 0;
     for (int j0 = 0; j0 < nvis; j0 += 64) {
       const int j = j0 + lane;
@@ -166,13 +318,13 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a, int R) {
     for (int j0 = 0; j0 < nvis; j0 += 64) {
       const int j = j0 + lane;
       const bool in = j < nvis;
-      const uint32_t kc = in ? keyc(j) : 0u, kr = in ? keyr(j) : 0u;
-      const uint64_t tiec = __ballot(in && kc == Tc);
-      const uint64_t tier = __ballot(in && kr == Tr);
+      const uint32_t kcv = in ? keyc(j) : 0u, krv = in ? keyr(j) : 0u;
+      const uint64_t tiec = __ballot(in && kcv == Tc);
+      const uint64_t tier = __ballot(in && krv == Tr);
       const int rankc = __popcll(tiec & lanemask_lt());
       const int rankr = __popcll(tier & lanemask_lt());
-      bool sel = in && ((kc > Tc) || (kc == Tc && rankc < needc) || (kr > Tr) ||
-                        (kr == Tr && rankr < needr) || j == i || (a.sink && j == 0));
+      const bool sel = in && ((kcv > Tc) || (kcv == Tc && rankc < needc) || (krv > Tr) ||
+                              (krv == Tr && rankr < needr) || j == i || (a.sink && j == 0));
       needc -= __popcll(tiec);
       needr -= __popcll(tier);
       const uint64_t m = __ballot(sel);
@@ -184,49 +336,57 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a, int R) {
   }
 }
 
-// Exclusive scan of counts into row_ptr and copy of rows into col_idx.
+// CSR assembly: one workgroup per 64 rows. The row offsets are the sum of all
+// earlier counts plus a scan inside the group; the copies are independent.
+constexpr int kCompactRows = 64;
+
+__device__ __forceinline__ int wave_isum(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
 __global__ __launch_bounds__(kThreads) void compact_kernel(const int32_t* __restrict__ counts,
                                                            const int32_t* __restrict__ lists,
                                                            int stride, int nrows,
                                                            int32_t* __restrict__ row_ptr,
                                                            int32_t* __restrict__ col_idx) {
-  __shared__ int sbuf[kThreads];
+  __shared__ int start[kCompactRows];
+  __shared__ int cnt_s[kCompactRows];
   __shared__ int wsum[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r0 = blockIdx.x * kThreads;
-  // base = sum of counts before this workgroup's rows
+  const int r0 = blockIdx.x * kCompactRows;
+  const int nr = min(kCompactRows, nrows - r0);
+  // sum of the counts of all earlier rows
   int s = 0;
   for (int x = tid; x < r0; x += kThreads) s += counts[x];
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  s = wave_isum(s);
   if (lane == 0) wsum[wave] = s;
   __syncthreads();
   const int base = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-  __syncthreads();
-  // inclusive scan of this workgroup's counts
-  const int row = r0 + tid;
-  const int c = row < nrows ? counts[row] : 0;
-  int x = c;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
+  // inclusive scan of this group's counts (wave 0)
+  if (wave == 0) {
+    const int c = lane < nr ? counts[r0 + lane] : 0;
+    int x = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane < nr) {
+      start[lane] = base + x - c;
+      cnt_s[lane] = c;
+      row_ptr[r0 + lane + 1] = base + x;
+    }
+    if (r0 == 0 && lane == 0) row_ptr[0] = 0;
   }
-  if (lane == 63) wsum[wave] = x;
   __syncthreads();
-  int off = 0;
-  for (int w = 0; w < wave; ++w) off += wsum[w];
-  const int incl = base + off + x;
-  if (row < nrows) row_ptr[row + 1] = incl;
-  if (row == 0) row_ptr[0] = 0;
-  sbuf[tid] = incl - c;  // exclusive start of each row
-  __syncthreads();
-  // copy: one wave per row
-  const int nr = min(kThreads, nrows - r0);
-  for (int rr = wave; rr < nr; rr += 4) {
-    const int rowi = r0 + rr;
-    const int cnt = counts[rowi];
-    const int start = sbuf[rr];
-    const int32_t* src = lists + (size_t)rowi * stride;
-    for (int e = lane; e < cnt; e += 64) col_idx[start + e] = src[e];
+  // copy: four threads per row
+  for (int t = tid; t < nr * 4; t += kThreads) {
+    const int rr = t >> 2, part = t & 3;
+    const int32_t* src = lists + (size_t)(r0 + rr) * stride;
+    const int c = cnt_s[rr], st = start[rr];
+    for (int e = part; e < c; e += 4) col_idx[st + e] = src[e];
   }
 }
 
@@ -236,8 +396,9 @@ __global__ void zero_row_ptr_kernel(int32_t* row_ptr) { row_ptr[0] = 0; }
 
 int select_rows_per_group(int nb, int D) {
   // LDS: rb[nb] + qrow[R*D] + red[16] + sc[R*pitch] floats
-  for (int R = kMaxRows; R >= 1; --R) {
-    const size_t bytes = ((size_t)nb + (size_t)R * D + 16 + (size_t)R * ((nb + 3) & ~3)) * 4;
+  for (int R = kSelRows; R >= 1; --R) {
+    const size_t bytes =
+        ((size_t)((nb + 3) & ~3) + (size_t)R * D + 16 + (size_t)R * ((nb + 3) & ~3)) * 4;
     if (bytes <= kLdsBudget) return R;
   }
   return 0;
@@ -250,14 +411,19 @@ rbs_status launch_select(const SelectArgs& a, hipStream_t st) {
   }
   const int R = select_rows_per_group(a.nb, a.D);
   if (R <= 0) return RBS_E_UNSUPPORTED;
-  const size_t shmem = ((size_t)a.nb + (size_t)R * a.D + 16 + (size_t)R * ((a.nb + 3) & ~3)) * 4;
+  const size_t shmem =
+      ((size_t)((a.nb + 3) & ~3) + (size_t)R * a.D + 16 + (size_t)R * ((a.nb + 3) & ~3)) * 4;
   dim3 grid((a.nb + R - 1) / R, a.Hkv);
-  hipLaunchKernelGGL(select_kernel, grid, dim3(kThreads), shmem, st, a, R);
+  if (a.nb <= 64 * kSelM && R == kSelRows)
+    hipLaunchKernelGGL(select_v2_kernel<kSelM>, grid, dim3(kThreads), shmem, st, a, R);
+  else
+    hipLaunchKernelGGL(select_long_kernel, grid, dim3(kThreads), shmem, st, a, R);
   rbs_status s = launch_status();
   if (s != RBS_OK) return s;
   const int nrows = a.Hkv * a.nb;
-  hipLaunchKernelGGL(compact_kernel, dim3((nrows + kThreads - 1) / kThreads), dim3(kThreads), 0,
-                     st, a.counts, a.lists, a.stride, nrows, a.row_ptr, a.col_idx);
+  hipLaunchKernelGGL(compact_kernel, dim3((nrows + kCompactRows - 1) / kCompactRows),
+                     dim3(kThreads), 0, st, a.counts, a.lists, a.stride, nrows, a.row_ptr,
+                     a.col_idx);
   return launch_status();
 }
 
