@@ -114,7 +114,9 @@ rbs_status rbs_select(const float* k_centroid, const float* k_radius, const floa
   select_sizes(n_blocks, keep_ratio_centroid, keep_ratio_rescue, sink, &per_head, &widest);
   const int64_t rows = (int64_t)n_kv_heads * n_blocks;
   const size_t counts_bytes = align256((size_t)rows * 4);
-  const size_t need = 256 + counts_bytes + align256((size_t)rows * widest * 4);
+  const size_t lists_bytes = align256((size_t)rows * widest * 4);
+  const size_t scores_bytes = align256(select_score_workspace(n_kv_heads, n_blocks));
+  const size_t need = 256 + counts_bytes + lists_bytes + scores_bytes;
   if (!workspace) {
     *workspace_bytes = need;
     return RBS_OK;
@@ -138,6 +140,9 @@ rbs_status rbs_select(const float* k_centroid, const float* k_radius, const floa
   a.col_idx = col_idx;
   a.counts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 256);
   a.lists = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 256 + counts_bytes);
+  a.scores = reinterpret_cast<float*>(static_cast<char*>(workspace) + 256 + counts_bytes +
+                                      lists_bytes);
+  a.rbeta = a.scores + (size_t)n_kv_heads * ((size_t)n_blocks * (n_blocks + 1) / 2);
   a.Hkv = n_kv_heads;
   a.nb = n_blocks;
   a.D = head_dim;

@@ -56,6 +56,8 @@ struct SelectArgs {
   int32_t* col_idx;
   int32_t* counts;   // workspace: [Hkv*nb]
   int32_t* lists;    // workspace: [Hkv*nb][stride]
+  float* scores;     // workspace: packed triangular centroid scores (nb <= 1024)
+  float* rbeta;      // workspace: r_j * beta_j per head (nb <= 1024)
   int Hkv, nb, D, stride;
   double rho_c, rho_r;
   int sink;
@@ -76,6 +78,7 @@ struct AttnArgs {
 rbs_status launch_attn_bf16_csr(const AttnArgs& a, hipStream_t st);
 rbs_status launch_attn_f32_csr(const AttnArgs& a, hipStream_t st);
 int select_rows_per_group(int nb, int D);
+size_t select_score_workspace(int Hkv, int nb);
 
 constexpr int kMaxSegments = 256;
 struct SegArgs {

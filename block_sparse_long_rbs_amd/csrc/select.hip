@@ -85,42 +85,51 @@ __device__ __forceinline__ uint32_t take_top(const uint32_t (&key)[M], int n, ui
   return bits;
 }
 
-constexpr int kSelRows = 8;   // query blocks per workgroup
-constexpr int kSelM = 16;     // candidates per lane held in registers (nb <= 1024)
+// ---------------------------------------------------------------------------
+// Two-kernel path for nb <= kTriMaxBlocks.
+//
+// Kernel A (scores): the centroid scores s[g][i][j] = q_rep[g][i] . c[g][j]
+// for j <= i form a lower triangle, cut into 64 x 64 tiles (one workgroup
+// each, equal work); every wave computes one 32 x 32 sub-tile with fp32
+// matrix-core products (v_mfma_f32_32x32x2_f32, fp32 inputs and
+// accumulation), operands read straight from L2. Scores go to a packed
+// triangular workspace (row i starts at i (i + 1) / 2). Hkv extra workgroups
+// derive each head's rescue coefficients and store r_j * beta_j.
+// Kernel B (rows): one wave per (g, i) ranks the row's keys held in
+// registers (centroid key and rescue key per candidate) and writes the
+// selected block list.
 
-// Scores for kSelRows query blocks x (i0 + kSelRows) key blocks, then one wave
-// per query block selects.
-template <int M>
-__global__ __launch_bounds__(kThreads) void select_v2_kernel(SelectArgs a, int R) {
-  extern __shared__ float smem[];
+constexpr int kTriMaxBlocks = 1024;
+constexpr int kTile = 64;
+
+__host__ __device__ __forceinline__ size_t tri_off(int i) { return (size_t)i * (i + 1) / 2; }
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void score_tiles_kernel(SelectArgs a) {
   const int g = blockIdx.y;
-  const int nb = a.nb, D = a.D;
-  // heaviest row groups first
-  const int grp = gridDim.x - 1 - blockIdx.x;
-  const int i0 = grp * R;
-  const int rows = min(R, nb - i0);
-  const int ncols = i0 + rows;
-  const int pitch = (ncols + 3) & ~3;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-
-  float* rb = smem;                  // [nb] r_j * beta_j
-  float* qrow = rb + ((nb + 3) & ~3);  // [R][D]
-  float* red = qrow + R * D;         // [16]
-  float* sc = red + 16;              // [R][pitch]
-
-  const float* rad = a.rad + (size_t)g * nb;
-  if (a.beta_in) {
-    const float* bi = a.beta_in + (size_t)g * nb;
-    for (int j = tid; j < ncols; j += kThreads) rb[j] = rad[j] * bi[j];
-    if (a.beta_out && grp == 0)
-      for (int j = tid; j < nb; j += kThreads) a.beta_out[(size_t)g * nb + j] = bi[j];
-  } else {
+  const int nb = a.nb;
+  const int nt = (nb + kTile - 1) / kTile;
+  const int ntiles = nt * (nt + 1) / 2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if ((int)blockIdx.x >= ntiles) {
+    // rescue coefficients of head g: beta = clamp((r - mean) / (max - mean), 0, 1)
+    __shared__ float red[8];
+    const float* rad = a.rad + (size_t)g * nb;
+    float* rb = a.rbeta + (size_t)g * nb;
+    if (a.beta_in) {
+      const float* bi = a.beta_in + (size_t)g * nb;
+      for (int j = tid; j < nb; j += kThreads) {
+        rb[j] = rad[j] * bi[j];
+        if (a.beta_out) a.beta_out[(size_t)g * nb + j] = bi[j];
+      }
+      return;
+    }
     float sum = 0.f, mx = 0.f;
     for (int j = tid; j < nb; j += kThreads) {
-      const float r = rad[j];
-      sum += r;
-      mx = fmaxf(mx, r);
+      sum += rad[j];
+      mx = fmaxf(mx, rad[j]);
     }
     sum = wave_sum(sum);
     mx = wave_max(mx);
@@ -130,88 +139,114 @@ __global__ __launch_bounds__(kThreads) void select_v2_kernel(SelectArgs a, int R
     const float top = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
     const float spread = top - mean;
     const bool ok = spread > 1e-6f * top;
-    const int jend = (a.beta_out && grp == 0) ? nb : ncols;
-    for (int j = tid; j < jend; j += kThreads) {
+    for (int j = tid; j < nb; j += kThreads) {
       const float b = ok ? fminf(fmaxf((rad[j] - mean) / spread, 0.f), 1.f) : 0.f;
-      if (j < ncols) rb[j] = rad[j] * b;
-      if (a.beta_out && grp == 0) a.beta_out[(size_t)g * nb + j] = b;
+      rb[j] = rad[j] * b;
+      if (a.beta_out) a.beta_out[(size_t)g * nb + j] = b;
     }
+    return;
   }
-  for (int x = tid; x < rows * D; x += kThreads) qrow[x] = a.qrep[((size_t)g * nb + i0) * D + x];
-  __syncthreads();
-
-  // ---- centroid scores: each thread a (R rows x 4 columns) register tile ----
-  const float* cen = a.cen + (size_t)g * nb * D;
-  for (int j0 = 4 * tid; j0 < ncols; j0 += 4 * kThreads) {
-    float acc[kSelRows][4];
-#pragma unroll
-    for (int r = 0; r < kSelRows; ++r)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
-    const float4* cj[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      cj[c] = reinterpret_cast<const float4*>(cen + (size_t)min(j0 + c, ncols - 1) * D);
-    for (int d4 = 0; d4 < D / 4; ++d4) {
-      float4 cv[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) cv[c] = cj[c][d4];
-#pragma unroll
-      for (int r = 0; r < kSelRows; ++r) {
-        if (r < rows) {
-          const float4 qv = reinterpret_cast<const float4*>(qrow + r * D)[d4];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            acc[r][c] = fmaf(qv.x, cv[c].x, acc[r][c]);
-            acc[r][c] = fmaf(qv.y, cv[c].y, acc[r][c]);
-            acc[r][c] = fmaf(qv.z, cv[c].z, acc[r][c]);
-            acc[r][c] = fmaf(qv.w, cv[c].w, acc[r][c]);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kSelRows; ++r)
-      if (r < rows)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (j0 + c < ncols) sc[r * pitch + j0 + c] = acc[r][c];
+  // tile index -> (row tile ti, column tile tj <= ti), heaviest rows first
+  int t = blockIdx.x;
+  int ti = nt - 1;
+  while (t > ti) { t -= ti + 1; --ti; }
+  const int tj = t;
+  const int i_base = ti * kTile + 32 * (wave >> 1);
+  const int j_base = tj * kTile + 32 * (wave & 1);
+  if (j_base > i_base + 31) return;  // sub-tile entirely above the diagonal
+  const int m32 = lane & 31, hh = lane >> 5;
+  const float* qrow = a.qrep + ((size_t)g * nb + min(i_base + m32, nb - 1)) * D + 4 * hh;
+  const float* crow = a.cen + ((size_t)g * nb + min(j_base + m32, nb - 1)) * D + 4 * hh;
+  f32x16_t acc = (f32x16_t){};
+#pragma unroll 4
+  for (int s8 = 0; s8 < D / 8; ++s8) {
+    const float4 qa = *reinterpret_cast<const float4*>(qrow + 8 * s8);
+    const float4 cb = *reinterpret_cast<const float4*>(crow + 8 * s8);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa.x, cb.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa.y, cb.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa.z, cb.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa.w, cb.w, acc, 0, 0, 0);
   }
-  __syncthreads();
-
-  // ---- per-row selection, one wave per query block ----
-  for (int r = wave; r < rows; r += kThreads / 64) {
-    const int i = i0 + r;
-    const int nvis = i + 1;
-    const float qn = a.qnorm[(size_t)g * nb + i];
-    const float* srow = sc + r * pitch;
-    uint32_t kc[M], kr[M];
+  float* sg = a.scores + (size_t)g * tri_off(nb);
+  const int j = j_base + m32;
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const int j = lane + 64 * m;
-      const bool in = j < nvis;
-      const float sv = in ? srow[j] : 0.f;
-      kc[m] = in ? order_key(sv) : 0u;
-      kr[m] = in ? order_key(fmaf(qn, rb[j], sv)) : 0u;
-    }
-    const int nc = budget(nvis, a.rho_c);
-    const int nr = budget(nvis, a.rho_r);
-    const uint32_t bc = take_top(kc, nc, nth_largest_regs(kc, nc));
-    const uint32_t br = take_top(kr, nr, nth_largest_regs(kr, nr));
-    int base = 0;
-    int32_t* out = a.lists + ((size_t)g * nb + i) * a.stride;
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const int j = lane + 64 * m;
-      const bool sel = j < nvis && ((((bc | br) >> m) & 1u) || j == i || (a.sink && j == 0));
-      const uint64_t msk = __ballot(sel);
-      const int pos = base + __popcll(msk & lanemask_lt());
-      if (sel && pos < a.stride) out[pos] = j;
-      base += __popcll(msk);
-    }
-    if (lane == 0) a.counts[(size_t)g * nb + i] = min(base, a.stride);
+  for (int r = 0; r < 16; ++r) {
+    const int i = i_base + 8 * (r >> 2) + 4 * hh + (r & 3);
+    if (i < nb && j <= i) sg[tri_off(i) + j] = acc[r];
   }
 }
+
+// Both branches' radix selects in one loop (independent ballot chains).
+template <int M>
+__device__ __forceinline__ void nth_largest_pair(const uint32_t (&ka)[M], int na,
+                                                 const uint32_t (&kb)[M], int nbr, uint32_t& Ta,
+                                                 uint32_t& Tb) {
+  Ta = 0;
+  Tb = 0;
+  bool da = false, db = false;
+  for (int bit = 31; bit >= 0 && !(da && db); --bit) {
+    const uint32_t ca = Ta | (1u << bit), cbv = Tb | (1u << bit);
+    int cnta = 0, cntb = 0;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      cnta += __popcll(__ballot(ka[m] >= ca));
+      cntb += __popcll(__ballot(kb[m] >= cbv));
+    }
+    if (!da && cnta >= na) {
+      Ta = ca;
+      da = (cnta == na);
+    }
+    if (!db && cntb >= nbr) {
+      Tb = cbv;
+      db = (cntb == nbr);
+    }
+  }
+}
+
+constexpr int kSelM = 16;   // candidates per lane held in registers (nb <= 1024)
+
+__global__ __launch_bounds__(kThreads) void select_rows_kernel(SelectArgs a) {
+  const int nb = a.nb;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // 4 rows per workgroup, all of one KV head; heaviest rows first
+  const int rows_per_g = (nb + 3) / 4;
+  const int g = blockIdx.x / rows_per_g;
+  const int i = nb - 1 - ((blockIdx.x % rows_per_g) * 4 + wave);
+  if (i < 0) return;
+  const int nvis = i + 1;
+  const float qn = a.qnorm[(size_t)g * nb + i];
+  const float* srow = a.scores + (size_t)g * tri_off(nb) + tri_off(i);
+  const float* rb = a.rbeta + (size_t)g * nb;
+  uint32_t kc[kSelM], kr[kSelM];
+#pragma unroll
+  for (int m = 0; m < kSelM; ++m) {
+    const int j = lane + 64 * m;
+    const bool in = j < nvis;
+    const float sv = in ? srow[j] : 0.f;
+    const float rbj = in ? rb[j] : 0.f;
+    kc[m] = in ? order_key(sv) : 0u;
+    kr[m] = in ? order_key(fmaf(qn, rbj, sv)) : 0u;
+  }
+  const int nc = budget(nvis, a.rho_c);
+  const int nr = budget(nvis, a.rho_r);
+  uint32_t Tc, Tr;
+  nth_largest_pair(kc, nc, kr, nr, Tc, Tr);
+  const uint32_t bits = take_top(kc, nc, Tc) | take_top(kr, nr, Tr);
+  int base = 0;
+  int32_t* out = a.lists + ((size_t)g * nb + i) * a.stride;
+#pragma unroll
+  for (int m = 0; m < kSelM; ++m) {
+    const int j = lane + 64 * m;
+    const bool sel = j < nvis && (((bits >> m) & 1u) || j == i || (a.sink && j == 0));
+    const uint64_t msk = __ballot(sel);
+    const int pos = base + __popcll(msk & lanemask_lt());
+    if (sel && pos < a.stride) out[pos] = j;
+    base += __popcll(msk);
+  }
+  if (lane == 0) a.counts[(size_t)g * nb + i] = min(base, a.stride);
+}
+
+constexpr int kLongRows = 8;  // query blocks per workgroup on the long-row path
 
 // Generic path for long rows (nb > 1024): keys are recomputed from LDS
 // on every pass instead of being held in registers.
@@ -396,7 +431,7 @@ __global__ void zero_row_ptr_kernel(int32_t* row_ptr) { row_ptr[0] = 0; }
 
 int select_rows_per_group(int nb, int D) {
   // LDS: rb[nb] + qrow[R*D] + red[16] + sc[R*pitch] floats
-  for (int R = kSelRows; R >= 1; --R) {
+  for (int R = kLongRows; R >= 1; --R) {
     const size_t bytes =
         ((size_t)((nb + 3) & ~3) + (size_t)R * D + 16 + (size_t)R * ((nb + 3) & ~3)) * 4;
     if (bytes <= kLdsBudget) return R;
@@ -404,20 +439,34 @@ int select_rows_per_group(int nb, int D) {
   return 0;
 }
 
+size_t select_score_workspace(int Hkv, int nb) {
+  return nb <= kTriMaxBlocks ? (size_t)Hkv * (tri_off(nb) + nb) * sizeof(float) : 0;
+}
+
 rbs_status launch_select(const SelectArgs& a, hipStream_t st) {
   if (a.nb == 0) {
     hipLaunchKernelGGL(zero_row_ptr_kernel, dim3(1), dim3(1), 0, st, a.row_ptr);
     return launch_status();
   }
-  const int R = select_rows_per_group(a.nb, a.D);
-  if (R <= 0) return RBS_E_UNSUPPORTED;
-  const size_t shmem =
-      ((size_t)((a.nb + 3) & ~3) + (size_t)R * a.D + 16 + (size_t)R * ((a.nb + 3) & ~3)) * 4;
-  dim3 grid((a.nb + R - 1) / R, a.Hkv);
-  if (a.nb <= 64 * kSelM && R == kSelRows)
-    hipLaunchKernelGGL(select_v2_kernel<kSelM>, grid, dim3(kThreads), shmem, st, a, R);
-  else
+  if (a.nb <= kTriMaxBlocks) {
+    const int nt = (a.nb + kTile - 1) / kTile;
+    dim3 g1(nt * (nt + 1) / 2 + 1, a.Hkv);
+    if (a.D == 64)
+      hipLaunchKernelGGL(score_tiles_kernel<64>, g1, dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL(score_tiles_kernel<128>, g1, dim3(kThreads), 0, st, a);
+    rbs_status s = launch_status();
+    if (s != RBS_OK) return s;
+    const int rows_per_g = (a.nb + 3) / 4;
+    hipLaunchKernelGGL(select_rows_kernel, dim3(rows_per_g * a.Hkv), dim3(kThreads), 0, st, a);
+  } else {
+    const int R = select_rows_per_group(a.nb, a.D);
+    if (R <= 0) return RBS_E_UNSUPPORTED;
+    const size_t shmem =
+        ((size_t)((a.nb + 3) & ~3) + (size_t)R * a.D + 16 + (size_t)R * ((a.nb + 3) & ~3)) * 4;
+    dim3 grid((a.nb + R - 1) / R, a.Hkv);
     hipLaunchKernelGGL(select_long_kernel, grid, dim3(kThreads), shmem, st, a, R);
+  }
   rbs_status s = launch_status();
   if (s != RBS_OK) return s;
   const int nrows = a.Hkv * a.nb;

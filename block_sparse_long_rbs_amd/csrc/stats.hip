@@ -17,6 +17,7 @@ namespace rbs {
 namespace {
 
 constexpr int kThreads = 256;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 template <typename T>
 struct Vec16;  // 16 bytes of T widened to floats
@@ -80,9 +81,11 @@ __global__ __launch_bounds__(kThreads) void block_stats_kernel(
         const T* p = qg + (size_t)to * row_stride + (size_t)vi * EPV;
         const size_t step = (size_t)TP * row_stride;
         int tt = to;
-#pragma unroll 4
+#pragma unroll 16
         for (; tt < L; tt += TP) {
-          uint4 w = *reinterpret_cast<const uint4*>(p);
+          // streamed once: non-temporal loads keep Q from displacing cached data
+          const u32x4_t wv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+          const uint4 w = make_uint4(wv.x, wv.y, wv.z, wv.w);
           float f[EPV];
           Vec16<T>::widen(w, f);
 #pragma unroll
