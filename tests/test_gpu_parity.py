@@ -46,6 +46,13 @@ def test_random_f32_block128():
     H.pipeline_case(w)
 
 
+def test_odd_gqa_ratio_bf16():
+    """GQA 3:1 (odd group, single-head workgroups) with a ragged tail."""
+    w = inputs.random_qkv(900, 6, 2, 128, "bf16", seed=13, block=128, name="gqa3_bf16_900",
+                          keep_ratio_centroid=0.4, keep_ratio_rescue=0.3, sink=True)
+    H.pipeline_case(w)
+
+
 def test_keep_ratio_one_is_dense_bf16():
     w = inputs.random_qkv(640, 8, 1, 128, "bf16", seed=5, block=128, name="dense_bf16_640",
                           keep_ratio_centroid=1.0, keep_ratio_rescue=1.0)
