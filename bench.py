@@ -55,7 +55,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the dense ratio and the Block-attention workload")
-    ap.add_argument("--cpu-rows", type=int, default=16)
+    ap.add_argument("--cpu-rows", type=int, default=256,
+                    help="(KV head, query block) rows of the oracle's attention to time")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -110,9 +111,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / K
-    t_stats = float(np.mean([ev[s][0].elapsed_time(ev[s][1]) for s in range(K)]))
-    t_sel = float(np.mean([ev[s][1].elapsed_time(ev[s][2]) for s in range(K)]))
-    t_attn = float(np.mean([ev[s][2].elapsed_time(ev[s][3]) for s in range(K)]))
+    per = {name: np.array([ev[s][a].elapsed_time(ev[s][a + 1]) for s in range(K)])
+           for a, name in enumerate(("stats", "select", "attn"))}
+    t_stats, t_sel, t_attn = (float(per[n].mean()) for n in ("stats", "select", "attn"))
     rp_h = rp.cpu().numpy().astype(np.int64)
     ci_h = ci[:int(rp_h[-1])].cpu().numpy()
     pairs = selected_pairs(rp_h, ci_h, S, B, Hkv) * G
@@ -140,10 +141,10 @@ def main():
         "config": {"workload": w.name, "seqlen": S, "n_q_heads": Hq, "n_kv_heads": Hkv,
                    "head_dim": D, "block": B, "keep_ratio_per_branch": w.keep_ratio_centroid,
                    "sink": w.sink, "beta": "derived", "seed": w.seed},
-        "roofline": {"bound": "mfma", "kernel": "attn_csr_bf16_kernel",
+        "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel<false> (CSR tiles)",
                      "achieved": round(attn_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": counted_traffic()},
         "phases": {
             "stats_ms": round(t_stats, 4), "select_ms": round(t_sel, 4),
             "attn_ms": round(t_attn, 4),
@@ -154,6 +155,10 @@ def main():
             "stats_select_hbm_frac": round((stats_bytes + select_bytes) /
                                            ((t_stats + t_sel) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "stats_bytes": stats_bytes, "select_bytes": select_bytes,
+            "percentiles_ms": {n: {"p10": round(float(np.percentile(v, 10)), 4),
+                                   "median": round(float(np.median(v)), 4),
+                                   "p90": round(float(np.percentile(v, 90)), 4)}
+                               for n, v in per.items()},
         },
     }
 
@@ -219,12 +224,37 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def counted_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE scaled by a 1 GiB copy), or None when
+    the kernel source has changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "attn_bf16_csr_mixture_128k_pmc.md")
+    src = os.path.join(ROOT, "block_sparse_long_rbs_amd", "csrc", "attn_bf16.hip")
+    try:
+        text = open(path).read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m = re.search(r"source_sha256: ([0-9a-f]{64}).*?hbm_bytes_per_launch: (\d+)", text, re.S)
+    if not m or m.group(1) != sha:
+        return None
+    return int(m.group(2))
+
+
 def cpu_baseline(w, flops_total, n_rows, log):
     """The float64 oracle on the host cores: stats and selection over the full
     workload, attention on n_rows sampled (KV head, query block) rows,
     extrapolated to the whole layer by their share of the attention flops."""
     from oracle import rbs_oracle as orc
-    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [(p.get("internal_api"), p.get("num_threads")) for p in threadpool_info()
+                if p.get("user_api") == "blas"]
+    except ImportError:
+        blas = []
+    cores = max([n for _, n in blas if n] or [len(os.sched_getaffinity(0))])
     t0 = time.perf_counter()
     c, r, qr, qn = orc.block_stats(w.q, w.k, w.n_kv_heads, w.block)
     t_stats = time.perf_counter() - t0
@@ -264,7 +294,7 @@ def cpu_baseline(w, flops_total, n_rows, log):
                        f"attention on {n_rows} random (KV head, query block) rows "
                        f"({t_attn_sample:.1f}s for {fl:.3g} flops), extrapolated by flops to "
                        f"the whole layer: {t_total:.0f}s per layer"),
-            "seconds_per_layer": round(t_total, 1)}
+            "seconds_per_layer": round(t_total, 1), "blas": blas}
 
 
 if __name__ == "__main__":
