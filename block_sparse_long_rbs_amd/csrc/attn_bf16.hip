@@ -8,8 +8,8 @@
 //  * Segment mode (Block-attention page, sections 2.1-2.5): a query tile of a
 //    non-final segment visits its own segment's key tiles up to the diagonal,
 //    a query tile of the final segment visits every key tile up to the
-//    diagonal; cached keys are rotated by their segment's RoPE offset while
-//    they are staged into LDS.
+//    diagonal; cached keys are rotated by their segment's RoPE offset once
+//    their tile has landed in LDS.
 //
 // Work decomposition. One workgroup = 4 waves = one query head h and one
 // query tile of 128 tokens; each wave owns 32 query rows; two workgroups
@@ -20,8 +20,10 @@
 //   O^T += V^T P^T (A = V^T read from LDS with the transposing load
 //                   ds_read_b64_tr_b16, B = P straight from the S registers)
 // Computing the transposed products leaves every lane holding one query row
-// (lane % 32) in both the score and the output accumulators, so the row max,
-// the rescale and the final normalisation need only one cross-half exchange.
+// (lane % 32) in both the score and the output accumulators; lanes l and l^32
+// share a row and combine through v_permlane32_swap. The running max is taken
+// from the row's first tile and kept while no exponential exceeds 2^64 (seen
+// through the tile's row sum), so the hot loop computes no per-tile max.
 //
 // Data movement. K and V tiles (32 KB each, 16-byte chunks XOR-swizzled per
 // row) go from HBM straight into LDS with global_load_lds_dwordx4, issued as
@@ -75,14 +77,15 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// One 16-byte-per-lane DMA from global memory into LDS at lds_addr + 16*lane.
-// Issued as inline asm so that the compiler does not treat it as a pending
-// LDS write (it would otherwise wait for every in-flight tile before each LDS
-// read); completion is awaited explicitly with wait_vmcnt.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+// One 16-byte-per-lane DMA from global memory (uniform base + per-lane 32-bit
+// byte offset) into LDS at lds_addr + 16*lane. Issued as inline asm so that
+// the compiler does not treat it as a pending LDS write (it would otherwise
+// wait for every in-flight tile before each LDS read); completion is awaited
+// explicitly with wait_vmcnt.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(gptr), "s"(lds_addr)
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
                : "memory", "m0");
 }
 
@@ -96,10 +99,10 @@ __device__ __forceinline__ int k_swz(int row) { return row & 15; }
 __device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
 
 // DMA one 128 x 128 bf16 tile (tokens key0.., one KV head; src points at that
-// head) into LDS. Each of the 4 waves issues 8 loads of 1 KB (4 rows); lane l
-// of a load lands at base + 16 l, so each lane fetches the logical chunk that
-// the swizzle puts there. Rows past the sequence end repeat the last row
-// (finite values; their scores are masked).
+// head's token 0) into LDS. Each of the 4 waves issues 8 loads of 1 KB (4
+// rows); lane l of a load lands at base + 16 l, so each lane fetches the
+// logical chunk that the swizzle puts there. Rows past the sequence end
+// repeat the last row (finite values; their scores are masked).
 template <bool IS_V>
 __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, size_t rs, int S,
                                          int key0, char* lds) {
@@ -108,19 +111,23 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, size_
   const int r4 = lane >> 4, pc = lane & 15;
   const uint32_t dst = lds_u32(lds) + wave * 8 * 1024;
   const int row0 = key0 + wave * 32;
+  const uint32_t rsb = (uint32_t)rs * 2;  // bytes per token row
   if (row0 + 32 <= S) {
     const uint16_t* base = src + (size_t)row0 * rs;
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int lc = IS_V ? (pc ^ (r4 << 2)) : (pc ^ (((it & 3) << 2) | r4));
-      dma16(base + (size_t)(it * 4) * rs + (r4 * rs + lc * 8), dst + it * 1024);
+      dma16(base + (size_t)(it * 4) * rs, r4 * rsb + lc * 16, dst + it * 1024);
     }
   } else {
+    // ragged end: rows are clamped to S - 1, offsets taken from min(row0, S - 1)
+    const int r0 = min(row0, S - 1);
+    const uint16_t* cbase = src + (size_t)r0 * rs;
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int lc = IS_V ? (pc ^ (r4 << 2)) : (pc ^ (((it & 3) << 2) | r4));
       const int tok = min(row0 + it * 4 + r4, S - 1);
-      dma16(src + (size_t)tok * rs + lc * 8, dst + it * 1024);
+      dma16(cbase, (uint32_t)(tok - r0) * rsb + lc * 16, dst + it * 1024);
     }
   }
 }
@@ -155,6 +162,18 @@ __device__ __forceinline__ void rotate_k_tile(char* Ks, const float2* rope) {
     *pa = make_uint4(ya[0], ya[1], ya[2], ya[3]);
     *pb = make_uint4(yb[0], yb[1], yb[2], yb[3]);
   }
+}
+
+// Lanes l and l^32 hold the same query row: combine their values.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Work unit decode: XCD-aware, heaviest (highest) query tiles first. The G
@@ -195,7 +214,7 @@ __device__ __forceinline__ void store_out(uint16_t* __restrict__ O, float* __res
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m32 = lane & 31, hh = lane >> 5;
   const int t = qt * TILE + wave * 32 + m32;
-  const float l = l_run + __shfl_xor(l_run, 32, 64);
+  const float l = pair_sum(l_run);
   if (t >= S || t < row_begin) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
   uint16_t* orow = O + ((size_t)t * Hq + h) * D;
@@ -297,7 +316,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
   f32x16_t o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = (f32x16_t){};
-  float m_run = -1e30f, l_run = 0.f;
+  float m_run = 0.f, l_run = 0.f;
+  bool first = true;
 
   // per-lane LDS offsets
   const int kx = m32 & 15;
@@ -357,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     lds_barrier();  // every wave is done with Ks
     if (jn >= 0) dma_tile<false>(Kg, rs, a.S, jn * TILE, Ks);
-    // ---- online softmax (base 2), lazy rescale by at most 2^8 ----
+    // ---- online softmax (base 2) ----
     if (j == u.qt) {
       // causal mask inside the diagonal tile; t is made opaque so that the
       // per-element predicates are not hoisted out of the tile loop
@@ -369,36 +389,50 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
         for (int r = 0; r < 16; ++r)
           if (kb * 32 + 8 * (r >> 2) + (r & 3) > t) s[kb][r] = -INFINITY;
     }
-    float mx = -INFINITY;
+    // The running max comes from the row's first tile; later tiles keep it
+    // as long as no exponential exceeds 2^64 (seen through the row sum, which
+    // also catches inf), else the max is raised and O rescaled (rare path).
+    auto tile_max = [&]() {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mt = mx * scale_log2;
-    const bool grow = mt > m_run + 8.f;
-    if (__ballot(grow)) {
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
-      m_run = grow ? mt : m_run;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      return pair_max(mx) * scale_log2;
+    };
+    if (first) {
+      m_run = tile_max();
+      first = false;
+    }
+    uint32_t pk[4][8];
+    auto exps = [&]() {
+      const float neg = -m_run;
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, neg));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], scale_log2, neg));
+          const uint32_t w = cvt_pk_bf16(p0, p1);
+          pk[kb][r >> 1] = w;
+          ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, ls, false);
+        }
+      return ls;
+    };
+    float ls = exps();
+    if (__ballot(!(ls <= 0x1p64f))) {
+      const float m_new = fmaxf(m_run, tile_max());
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      ls = exps();
     }
-    const float neg = -m_run;
-    uint32_t pk[4][8];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, neg));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], scale_log2, neg));
-        const uint32_t w = cvt_pk_bf16(p0, p1);
-        pk[kb][r >> 1] = w;
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, l_run,
-                                                false);
-      }
+    l_run += ls;
     if (jn >= 0) wait_vmcnt<8>(); else wait_vmcnt<0>();  // V(j) has landed
     lds_barrier();
     // ---- O^T += V^T P^T (four independent accumulators in turn) ----
