@@ -115,3 +115,45 @@ def test_csr_entries_outside_the_causal_range_are_skipped():
     o, _ = orc.blocksparse_attention(w.q, w.k, w.v, 128, rp, ci)
     d = np.abs(H.to_host(out) - o)
     assert d.max() <= H.TOL_BF16_MAX and d.mean() <= H.TOL_BF16_MEAN
+
+
+def test_late_dominant_key_raises_the_running_max():
+    """A key in block 1 gives the queries of block 3 logits about 70 (base 2)
+    above everything in block 0, the first block of their CSR row: the kernel
+    must raise its running max and rescale the partial output (its rare path).
+    Listing the dominant block first must give the same result."""
+    S, Hq, Hkv, D, B = 512, 8, 2, 128, 128
+    w = inputs.random_qkv(S, Hq, Hkv, D, "bf16", seed=31, block=B, name="late_max")
+    rng = np.random.default_rng(5)
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    q = w.q.astype(np.float64)
+    q[3 * B:4 * B, 0:Hq // Hkv] += 3.0 * u          # group 0 queries of block 3 lean along u
+    k = w.k.astype(np.float64)
+    k[200, 0] = 200.0 * u                            # block 1, group 0: dominant key
+    w.q = inputs.bf16_round(q.astype(np.float32))
+    w.k = inputs.bf16_round(k.astype(np.float32))
+    t = device.upload(w)
+    rp, ci = orc.dense_causal_selection(Hkv, S // B)
+    o, lse_o = orc.blocksparse_attention(w.q, w.k, w.v, B, rp, ci)
+    # the logits really do exceed the first block's max by more than 64 (base 2)
+    scale_log2 = 1.4426950408889634 / np.sqrt(D)
+    qq = w.q[3 * B:4 * B, 0].astype(np.float64)
+    first = (qq @ w.k[0:B, 0].astype(np.float64).T).max(axis=1) * scale_log2
+    late = (qq @ w.k[200, 0].astype(np.float64)) * scale_log2
+    assert (late - first).max() > 64
+    for order in ("ascending", "dominant first"):
+        ci_o = ci.copy()
+        if order != "ascending":
+            for r in range(len(rp) - 1):
+                row = list(ci_o[rp[r]:rp[r + 1]])
+                if 1 in row:
+                    row.remove(1)
+                    ci_o[rp[r]:rp[r + 1]] = [1] + row
+        a, b = H.csr_to_device(rp, ci_o)
+        out, lse = rbs.blocksparse_attn_fwd(t["q"], t["k"], t["v"], B, a, b, want_lse=True)
+        d = np.abs(H.to_host(out) - o)
+        H.say(f"  {order}: max-abs {d.max():.3e} mean-abs {d.mean():.3e}")
+        assert d.max() <= H.TOL_BF16_MAX and d.mean() <= H.TOL_BF16_MEAN, order
+        dl = np.abs(lse.cpu().numpy() - lse_o)
+        assert dl.max() <= 2e-2, (order, dl.max())
