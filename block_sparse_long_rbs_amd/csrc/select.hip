@@ -157,15 +157,20 @@ __global__ __launch_bounds__(kThreads) void score_tiles_kernel(SelectArgs a) {
   const int m32 = lane & 31, hh = lane >> 5;
   const float* qrow = a.qrep + ((size_t)g * nb + min(i_base + m32, nb - 1)) * D + 4 * hh;
   const float* crow = a.cen + ((size_t)g * nb + min(j_base + m32, nb - 1)) * D + 4 * hh;
-  f32x16_t acc = (f32x16_t){};
-#pragma unroll 4
+  // all operand loads in flight at once (the tile is latency bound)
+  float4 qa[D / 8], cb[D / 8];
+#pragma unroll
   for (int s8 = 0; s8 < D / 8; ++s8) {
-    const float4 qa = *reinterpret_cast<const float4*>(qrow + 8 * s8);
-    const float4 cb = *reinterpret_cast<const float4*>(crow + 8 * s8);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa.x, cb.x, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa.y, cb.y, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa.z, cb.z, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa.w, cb.w, acc, 0, 0, 0);
+    qa[s8] = *reinterpret_cast<const float4*>(qrow + 8 * s8);
+    cb[s8] = *reinterpret_cast<const float4*>(crow + 8 * s8);
+  }
+  f32x16_t acc = (f32x16_t){};
+#pragma unroll
+  for (int s8 = 0; s8 < D / 8; ++s8) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[s8].x, cb[s8].x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[s8].y, cb[s8].y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[s8].z, cb[s8].z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[s8].w, cb[s8].w, acc, 0, 0, 0);
   }
   float* sg = a.scores + (size_t)g * tri_off(nb);
   const int j = j_base + m32;
@@ -205,21 +210,18 @@ __device__ __forceinline__ void nth_largest_pair(const uint32_t (&ka)[M], int na
 
 constexpr int kSelM = 16;   // candidates per lane held in registers (nb <= 1024)
 
-__global__ __launch_bounds__(kThreads) void select_rows_kernel(SelectArgs a) {
+// One row (g, i): its i + 1 candidates, M per lane (64 M >= i + 1).
+template <int M>
+__device__ __forceinline__ void select_row(const SelectArgs& a, int g, int i) {
   const int nb = a.nb;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // 4 rows per workgroup, all of one KV head; heaviest rows first
-  const int rows_per_g = (nb + 3) / 4;
-  const int g = blockIdx.x / rows_per_g;
-  const int i = nb - 1 - ((blockIdx.x % rows_per_g) * 4 + wave);
-  if (i < 0) return;
+  const int lane = threadIdx.x & 63;
   const int nvis = i + 1;
   const float qn = a.qnorm[(size_t)g * nb + i];
   const float* srow = a.scores + (size_t)g * tri_off(nb) + tri_off(i);
   const float* rb = a.rbeta + (size_t)g * nb;
-  uint32_t kc[kSelM], kr[kSelM];
+  uint32_t kc[M], kr[M];
 #pragma unroll
-  for (int m = 0; m < kSelM; ++m) {
+  for (int m = 0; m < M; ++m) {
     const int j = lane + 64 * m;
     const bool in = j < nvis;
     const float sv = in ? srow[j] : 0.f;
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void select_rows_kernel(SelectArgs a) {
   int base = 0;
   int32_t* out = a.lists + ((size_t)g * nb + i) * a.stride;
 #pragma unroll
-  for (int m = 0; m < kSelM; ++m) {
+  for (int m = 0; m < M; ++m) {
     const int j = lane + 64 * m;
     const bool sel = j < nvis && (((bits >> m) & 1u) || j == i || (a.sink && j == 0));
     const uint64_t msk = __ballot(sel);
@@ -244,6 +246,19 @@ __global__ __launch_bounds__(kThreads) void select_rows_kernel(SelectArgs a) {
     base += __popcll(msk);
   }
   if (lane == 0) a.counts[(size_t)g * nb + i] = min(base, a.stride);
+}
+
+__global__ __launch_bounds__(kThreads) void select_rows_kernel(SelectArgs a) {
+  const int nb = a.nb;
+  const int wave = threadIdx.x >> 6;
+  // 4 rows per workgroup, all of one KV head; heaviest rows first
+  const int rows_per_g = (nb + 3) / 4;
+  const int g = blockIdx.x / rows_per_g;
+  const int i = nb - 1 - ((blockIdx.x % rows_per_g) * 4 + wave);
+  if (i < 0) return;
+  if (i < 4 * 64) select_row<4>(a, g, i);
+  else if (i < 8 * 64) select_row<8>(a, g, i);
+  else select_row<kSelM>(a, g, i);
 }
 
 constexpr int kLongRows = 8;  // query blocks per workgroup on the long-row path
