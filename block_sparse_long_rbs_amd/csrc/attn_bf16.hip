@@ -356,6 +356,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
       }
     }
     // ---- S^T = K Q^T (four independent accumulators in turn) ----
+    // Wave priority: matrix phases win issue over the other workgroup's
+    // softmax on the same SIMD (P.V highest, so a tile's output accumulation
+    // is not held up behind the next tile's scores).
+    __builtin_amdgcn_s_setprio(1);
     f32x16_t s[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) s[kb] = (f32x16_t){};
@@ -375,6 +379,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_s_setprio(0);
     lds_barrier();  // every wave is done with Ks
     if (jn >= 0) dma_tile<false>(Kg, rs, a.S, jn * TILE, Ks);
     // ---- online softmax (base 2) ----
@@ -436,6 +441,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
     if (jn >= 0) wait_vmcnt<8>(); else wait_vmcnt<0>();  // V(j) has landed
     lds_barrier();
     // ---- O^T += V^T P^T (four independent accumulators in turn) ----
+    __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int c = 0; c < 8; ++c)
 #pragma unroll
@@ -459,6 +465,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_s_setprio(0);
     lds_barrier();  // every wave is done with Vs
     if (jn >= 0) dma_tile<true>(Vg, rs, a.S, jn * TILE, Vs);
     j = jn;
