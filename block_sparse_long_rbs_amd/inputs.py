@@ -269,6 +269,27 @@ def rag_bf16_31k(seed: int = 5) -> Workload:
     return rag_layout(seed=seed)
 
 
+
+def synthetic_block_stats(n_kv_heads: int, n_blocks: int, head_dim: int, seed: int = 0,
+                          beta_given: bool = False):
+    """Block statistics drawn directly (for testing the selection on its own at
+    sizes the attention workloads do not reach, e.g. more than 1,024 blocks).
+
+    Centroids are a per-block random mean scaled by a lognormal factor, the
+    representative queries N(0, I), their norms the float32 Euclidean norms,
+    radii positive with a heavy upper tail. Returns float32 arrays
+    (centroid, radius, q_rep, q_rep_norm, beta or None)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shape = (n_kv_heads, n_blocks, head_dim)
+    scale = np.exp(0.3 * rng.standard_normal((n_kv_heads, n_blocks, 1))).astype(np.float32)
+    cen = (rng.standard_normal(shape, dtype=np.float32) * scale).astype(np.float32)
+    qrep = rng.standard_normal(shape, dtype=np.float32)
+    qn = np.sqrt((qrep.astype(np.float64) ** 2).sum(-1)).astype(np.float32)
+    rad = (1.0 + np.abs(rng.standard_normal((n_kv_heads, n_blocks), dtype=np.float32)) * 2.0
+           + (rng.random((n_kv_heads, n_blocks)) < 0.1) * 6.0).astype(np.float32)
+    beta = rng.random((n_kv_heads, n_blocks)).astype(np.float32) if beta_given else None
+    return cen, rad, qrep, qn, beta
+
 WORKLOADS = {
     "tiny_f32_1k": tiny_f32_1k,
     "needle_bf16_8k": needle_bf16_8k,

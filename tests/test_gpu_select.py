@@ -1,0 +1,42 @@
+"""GPU parity of rbs_select on its own, on directly drawn block statistics:
+both selection paths (register-held rows for up to 1,024 blocks, LDS rows
+beyond), derived and given beta, with and without the sink. Sets must equal
+the oracle's outside its threshold band; derived beta within 1e-5."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_rbs_amd as rbs
+from block_sparse_long_rbs_amd import inputs
+from oracle import rbs_oracle as orc
+
+import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("nb,D,rho_c,rho_r,sink,beta_given,seed", [
+    (1024, 128, 0.05, 0.05, True, False, 1),    # largest register-path size
+    (1032, 64, 0.05, 0.08, True, False, 2),     # just past it: LDS path
+    (1500, 128, 0.1, 0.03, False, True, 3),     # LDS path, beta given
+    (2100, 128, 0.02, 0.02, True, False, 4),    # long rows
+    (300, 64, 0.5, 0.25, False, False, 5),      # short rows, large budgets
+])
+def test_select_matches_oracle(nb, D, rho_c, rho_r, sink, beta_given, seed):
+    Hkv = 2
+    cen, rad, qrep, qn, beta = inputs.synthetic_block_stats(Hkv, nb, D, seed, beta_given)
+    H.say(f"[select] nb={nb} D={D} rho=({rho_c},{rho_r}) sink={sink} beta_given={beta_given}")
+    dev = lambda x: torch.from_numpy(x).cuda()
+    rp, ci, beta_out = rbs.rbs_select(dev(cen), dev(rad), dev(qrep), dev(qn), rho_c, rho_r,
+                                      sink=sink, beta=dev(beta) if beta is not None else None,
+                                      want_beta=True)
+    torch.cuda.synchronize()
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    ci_h = ci.cpu().numpy()[:rp_h[-1]]
+    b = beta.astype(np.float64) if beta is not None else orc.derive_beta(rad.astype(np.float64))
+    sel = orc.select(cen.astype(np.float64), rad.astype(np.float64), qrep.astype(np.float64),
+                     qn.astype(np.float64), b, rho_c, rho_r, sink)
+    diff, total = H.compare_selection(sel, rp_h, ci_h, Hkv, nb, sink)
+    H.say(f"  {diff}/{total} rows differ, all inside the threshold band")
+    np.testing.assert_allclose(beta_out.cpu().numpy(), sel.beta, atol=1e-5)
+    assert rp_h[-1] == len(sel.col_idx) or diff > 0
