@@ -198,11 +198,13 @@ def main():
         outr = torch.empty_like(tr["q"])
         args_r = (tr["q"], tr["k"], tr["v"], wr.seg_start.tolist(), wr.k_rerotate.tolist(),
                   wr.rope_theta)
+        wsr = torch.empty(max(1, rbs.block_mask_workspace_bytes(*args_r)), dtype=torch.uint8,
+                          device="cuda")
         for _ in range(3):
-            rbs.block_mask_attn_fwd(*args_r, out=outr)
+            rbs.block_mask_attn_fwd(*args_r, out=outr, workspace=wsr)
         e0.record(stream)
         for _ in range(10):
-            rbs.block_mask_attn_fwd(*args_r, out=outr)
+            rbs.block_mask_attn_fwd(*args_r, out=outr, workspace=wsr)
         e1.record(stream)
         torch.cuda.synchronize()
         t_bm = e0.elapsed_time(e1) / 10
@@ -217,7 +219,7 @@ def main():
                                         "tflops": round(fl_bm / (t_bm * 1e-3) / 1e12, 1),
                                         "flops": fl_bm}
         log(f"block-mask RAG 31K: {t_bm:.3f} ms, {fl_bm / (t_bm * 1e-3) / 1e12:.1f} TFLOP/s")
-        del tr, outr
+        del tr, outr, wsr
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, flops, args.cpu_rows, log)

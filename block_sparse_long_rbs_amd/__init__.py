@@ -5,8 +5,8 @@ include/rbs.h); this package holds the ctypes binding, a host-to-device
 upload helper and the seeded synthetic workloads. The shared library is
 loaded on first use; a missing library raises, there is no fallback.
 """
-from ._lib import (RbsError, block_mask_attn_fwd, blocksparse_attn_fwd, lib, rbs_block_stats,
-                   rbs_select, rbs_select_capacity)
+from ._lib import (RbsError, block_mask_attn_fwd, block_mask_workspace_bytes,
+                   blocksparse_attn_fwd, lib, rbs_block_stats, rbs_select, rbs_select_capacity)
 
-__all__ = ["RbsError", "block_mask_attn_fwd", "blocksparse_attn_fwd", "lib", "rbs_block_stats",
-           "rbs_select", "rbs_select_capacity"]
+__all__ = ["RbsError", "block_mask_attn_fwd", "block_mask_workspace_bytes",
+           "blocksparse_attn_fwd", "lib", "rbs_block_stats", "rbs_select", "rbs_select_capacity"]

@@ -40,7 +40,7 @@ _SIGS = {
     "block_mask_attn_fwd": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
                                            _c_i32, _c_i32, ctypes.POINTER(_c_i32),
                                            ctypes.POINTER(_c_i32), _c_f32, _c_i32, _c_f32, _vp,
-                                           _vp, _vp]),
+                                           _vp, _vp, ctypes.POINTER(ctypes.c_size_t), _vp]),
 }
 
 _lib = None
@@ -175,20 +175,49 @@ def blocksparse_attn_fwd(q, k, v, block: int, row_ptr, col_idx, softmax_scale: f
     return out, lse
 
 
-def block_mask_attn_fwd(q, k_cached, v, seg_start: Sequence[int], k_rerotate: Sequence[int],
-                        rope_theta: float, q_row_begin: int = 0, softmax_scale: float = 0.0,
-                        want_lse: bool = False, out: Optional[torch.Tensor] = None):
-    """Block-attention prefill with RoPE re-encoding of cached keys -> (out, lse or None)."""
-    _need_cuda(q, k_cached, v)
+def _bmask_args(q, k_cached, v, seg_start, k_rerotate, rope_theta, q_row_begin, softmax_scale,
+                out, lse):
     S, Hq, D = q.shape
     Hkv = k_cached.shape[1]
     n_seg = len(seg_start) - 1
     ss = (_c_i32 * (n_seg + 1))(*[int(x) for x in seg_start])
     rr = (_c_i32 * max(n_seg, 1))(*[int(x) for x in k_rerotate])
+    return (_dtype_code(q), q.data_ptr(), k_cached.data_ptr(), v.data_ptr(), S, Hq, Hkv, D, n_seg,
+            ss, rr, rope_theta, q_row_begin, softmax_scale, _ptr(out), _ptr(lse))
+
+
+def block_mask_workspace_bytes(q, k_cached, v, seg_start: Sequence[int],
+                               k_rerotate: Sequence[int], rope_theta: float,
+                               q_row_begin: int = 0) -> int:
+    """Workspace bytes block_mask_attn_fwd needs for this layout (size query)."""
+    # a size query enqueues nothing; q stands in for the output pointer, which
+    # is only checked for alignment
+    args = _bmask_args(q, k_cached, v, seg_start, k_rerotate, rope_theta, q_row_begin, 0.0, q,
+                       None)
+    need = ctypes.c_size_t(0)
+    _check("block_mask_attn_fwd", lib().block_mask_attn_fwd(*args, None, ctypes.byref(need), None))
+    return need.value
+
+
+def block_mask_attn_fwd(q, k_cached, v, seg_start: Sequence[int], k_rerotate: Sequence[int],
+                        rope_theta: float, q_row_begin: int = 0, softmax_scale: float = 0.0,
+                        want_lse: bool = False, out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None):
+    """Block-attention prefill with RoPE re-encoding of cached keys -> (out, lse or None).
+    The workspace (re-encoded keys; partial results of the final block's split
+    rows) is allocated when not given or too small."""
+    _need_cuda(q, k_cached, v)
+    S, Hq, D = q.shape
     if out is None:
         out = torch.empty_like(q)
     lse = torch.empty((Hq, S), dtype=torch.float32, device=q.device) if want_lse else None
+    args = _bmask_args(q, k_cached, v, seg_start, k_rerotate, rope_theta, q_row_begin,
+                       softmax_scale, out, lse)
+    need = ctypes.c_size_t(0)
+    _check("block_mask_attn_fwd", lib().block_mask_attn_fwd(*args, None, ctypes.byref(need), None))
+    if workspace is None or workspace.numel() < max(need.value, 1):
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
+    wsz = ctypes.c_size_t(workspace.numel())
     _check("block_mask_attn_fwd", lib().block_mask_attn_fwd(
-        _dtype_code(q), q.data_ptr(), k_cached.data_ptr(), v.data_ptr(), S, Hq, Hkv, D, n_seg, ss,
-        rr, rope_theta, q_row_begin, softmax_scale, out.data_ptr(), _ptr(lse), _stream(q)))
+        *args, workspace.data_ptr(), ctypes.byref(wsz), _stream(q)))
     return out, lse

@@ -46,6 +46,12 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 }  // namespace
 
+namespace {
+// Key tiles per chunk when the final block's rows are split (see
+// block_mask_attn_fwd).
+constexpr int kChunkTiles = 64;
+}  // namespace
+
 extern "C" {
 
 const char* rbs_status_string(rbs_status s) {
@@ -194,12 +200,13 @@ rbs_status block_mask_attn_fwd(rbs_dtype dt, const void* q, const void* k_cached
                                int32_t n_kv_heads, int32_t head_dim, int32_t n_segments,
                                const int32_t* seg_start, const int32_t* k_rerotate,
                                float rope_theta, int32_t q_row_begin, float softmax_scale,
-                               void* out, float* lse, void* stream) {
+                               void* out, float* lse, void* workspace, size_t* workspace_bytes,
+                               void* stream) {
   if (dt != RBS_DT_BF16 && dt != RBS_DT_F32) return RBS_E_ARG;
   if (seqlen < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || n_segments <= 0)
     return RBS_E_ARG;
   if (n_q_heads % n_kv_heads != 0) return RBS_E_ARG;
-  if (!seg_start || !k_rerotate) return RBS_E_ARG;
+  if (!seg_start || !k_rerotate || !workspace_bytes) return RBS_E_ARG;
   if (!aligned(q, 16) || !aligned(k_cached, 16) || !aligned(v, 16) || !aligned(out, 16) ||
       (lse && !aligned(lse, 4)))
     return RBS_E_ARG;
@@ -216,10 +223,40 @@ rbs_status block_mask_attn_fwd(rbs_dtype dt, const void* q, const void* k_cached
   for (int p = 0; p < n_segments; ++p)
     if (seg_start[p] % 128 != 0) return RBS_E_UNSUPPORTED;
   if ((int64_t)seqlen * n_q_heads * head_dim > ((int64_t)1 << 40)) return RBS_E_UNSUPPORTED;
+  // Work plan. (1) When any segment has a nonzero offset, the keys are
+  // re-encoded once into the workspace and the attention reads that copy.
+  // (2) The final block's query tiles see every earlier tile; when they see
+  // many, each one's key range is cut into chunks of kChunkTiles tiles run by
+  // separate workgroups (placed first in the launch, ahead of the other
+  // tiles), whose partial results a second kernel merges; otherwise these
+  // few long rows would set the kernel's length.
+  bool rotate = false;
+  for (int p = 0; p < n_segments; ++p) rotate = rotate || k_rerotate[p] != 0;
+  rotate = rotate && q_row_begin < seqlen;
+  const int nq = (seqlen + 127) / 128;
+  const int qt_begin = q_row_begin / 128;
+  const int fs = seg_start[n_segments - 1] / 128;  // first tile of the final block
+  const int final_lo = fs > qt_begin ? fs : qt_begin;
+  const bool split = seqlen > 0 && q_row_begin < seqlen && final_lo < nq &&
+                     final_lo + 1 >= 2 * kChunkTiles;
+  const int chunks = split ? (nq + kChunkTiles - 1) / kChunkTiles : 0;
+  const size_t keys_bytes =
+      rotate ? align256((size_t)seqlen * n_kv_heads * head_dim * 2) : 0;
+  const size_t table_bytes = rotate ? align256((size_t)n_segments * (head_dim / 2) * 8) : 0;
+  const size_t part_bytes =
+      split ? (size_t)(nq - final_lo) * n_q_heads * chunks * 128 * kPartRow * sizeof(float) : 0;
+  const size_t need = keys_bytes + table_bytes + part_bytes;
+  if (!workspace) {
+    *workspace_bytes = need;
+    return RBS_OK;
+  }
+  if (*workspace_bytes < need) return RBS_E_CAPACITY;
+  if (need > 0 && !aligned(workspace, 256)) return RBS_E_ARG;
   if (seqlen == 0 || q_row_begin == seqlen) return RBS_OK;
+  char* ws = static_cast<char*>(workspace);
   AttnArgs a;
   a.q = q;
-  a.k = k_cached;
+  a.k = rotate ? ws : k_cached;
   a.v = v;
   a.out = out;
   a.lse = lse;
@@ -238,7 +275,28 @@ rbs_status block_mask_attn_fwd(rbs_dtype dt, const void* q, const void* k_cached
   s.theta = rope_theta;
   for (int p = 0; p <= n_segments; ++p) s.start[p] = seg_start[p];
   for (int p = 0; p < n_segments; ++p) s.rerot[p] = k_rerotate[p];
-  return launch_attn_segments(a, s, as_stream(stream));
+  hipStream_t st = as_stream(stream);
+  if (rotate) {
+    rbs_status r = launch_rerotate(k_cached, ws, reinterpret_cast<float2*>(ws + keys_bytes),
+                                   seqlen, n_kv_heads, s, st);
+    if (r != RBS_OK) return r;
+  }
+  if (!split) {
+    s.rest_lo = qt_begin;
+    s.rest_hi = nq;
+    return launch_attn_segments(a, s, st);
+  }
+  s.qt_lo = final_lo;
+  s.qt_hi = nq;
+  s.chunks = chunks;
+  s.chunk_tiles = kChunkTiles;
+  s.part = reinterpret_cast<float*>(ws + keys_bytes + table_bytes);
+  s.grid_split = attn_split_grid(n_q_heads, n_kv_heads, nq - final_lo, chunks);
+  s.rest_lo = qt_begin;
+  s.rest_hi = fs < nq ? fs : nq;
+  rbs_status r = launch_attn_segments(a, s, st);
+  if (r != RBS_OK) return r;
+  return launch_attn_combine(a, s, st);
 }
 
 }  // extern "C"

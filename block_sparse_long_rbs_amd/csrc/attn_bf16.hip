@@ -8,8 +8,9 @@
 //  * Segment mode (Block-attention page, sections 2.1-2.5): a query tile of a
 //    non-final segment visits its own segment's key tiles up to the diagonal,
 //    a query tile of the final segment visits every key tile up to the
-//    diagonal; cached keys are rotated by their segment's RoPE offset once
-//    their tile has landed in LDS.
+//    diagonal (the keys arrive already re-encoded, see rope.hip). The final
+//    segment's long rows can be cut into key-range chunks whose partial
+//    results attn_combine_kernel merges.
 //
 // Work decomposition. One workgroup = 4 waves = one query head h and one
 // query tile of 128 tokens; each wave owns 32 query rows; two workgroups
@@ -132,38 +133,6 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, size_
   }
 }
 
-// Rotate a landed K tile in place by one RoPE offset (rotate-half pairs
-// (d, d + 64); cos/sin per frequency in `rope`). Thread tid takes chunk pair
-// (8cp.., 64 + 8cp..) of rows tid/8 + 32 it, in the swizzled layout.
-__device__ __forceinline__ void rotate_k_tile(char* Ks, const float2* rope) {
-  const int tid = threadIdx.x;
-  const int cp = tid & 7, rr = tid >> 3;
-  float2 cs[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) cs[e] = rope[8 * cp + e];
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int row = rr + 32 * it;
-    const int sw = k_swz(row);
-    uint4* pa = reinterpret_cast<uint4*>(Ks + row * ROWB + ((cp ^ sw) << 4));
-    uint4* pb = reinterpret_cast<uint4*>(Ks + row * ROWB + (((cp + 8) ^ sw) << 4));
-    const uint4 A = *pa, B = *pb;
-    const uint32_t aw[4] = {A.x, A.y, A.z, A.w};
-    const uint32_t bw[4] = {B.x, B.y, B.z, B.w};
-    uint32_t ya[4], yb[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float x10 = bf16_lo(aw[w]), x11 = bf16_hi(aw[w]);
-      const float x20 = bf16_lo(bw[w]), x21 = bf16_hi(bw[w]);
-      const float2 c0 = cs[2 * w], c1 = cs[2 * w + 1];
-      ya[w] = cvt_pk_bf16(x10 * c0.x - x20 * c0.y, x11 * c1.x - x21 * c1.y);
-      yb[w] = cvt_pk_bf16(x20 * c0.x + x10 * c0.y, x21 * c1.x + x11 * c1.y);
-    }
-    *pa = make_uint4(ya[0], ya[1], ya[2], ya[3]);
-    *pb = make_uint4(yb[0], yb[1], yb[2], yb[3]);
-  }
-}
-
 // Lanes l and l^32 hold the same query row: combine their values.
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
@@ -177,21 +146,24 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 // Work unit decode: XCD-aware, heaviest (highest) query tiles first. The G
-// heads of one (KV head, query tile) unit get neighbouring slots on one XCD.
+// heads (times the key-range chunks, if any) of one (KV head, query tile)
+// unit get neighbouring slots on one XCD.
 struct Unit {
-  int g, h, qt;
+  int g, h, qt, c;
 };
-__device__ __forceinline__ bool decode_unit(int G, int Hkv, int n_qt, int qt_begin, Unit& u) {
-  const int x = blockIdx.x;
+__device__ __forceinline__ bool decode_unit(int x, int G, int Hkv, int qt_lo, int qt_hi, int C,
+                                            Unit& u) {
+  const int per = G * C;
   const int xcd = x & 7;
   const int slot = x >> 3;
-  const int hg = slot % G;
-  const int uo = (slot / G) * 8 + xcd;
-  const int n_units = Hkv * (n_qt - qt_begin);
+  const int hg = slot % per;
+  const int uo = (slot / per) * 8 + xcd;
+  const int n_units = Hkv * (qt_hi - qt_lo);
   if (uo >= n_units) return false;
-  u.qt = n_qt - 1 - uo / Hkv;
+  u.qt = qt_hi - 1 - uo / Hkv;
   u.g = uo % Hkv;
-  u.h = u.g * G + hg;
+  u.h = u.g * G + hg % G;
+  u.c = hg / G;
   return true;
 }
 
@@ -231,6 +203,80 @@ __device__ __forceinline__ void store_out(uint16_t* __restrict__ O, float* __res
     lse[(size_t)h * S + t] = l > 0.f ? (m_run + __log2f(l)) * 0.69314718055994530942f : -INFINITY;
 }
 
+// Unnormalised partial result of one key-range chunk: for each of the tile's
+// 128 query rows, O (D floats, not yet divided by the row sum), the running
+// max m (base 2, scaled) and the row sum l.
+__device__ __forceinline__ void store_part(float* __restrict__ part, const f32x16_t* o, float m_run,
+                                           float l_run) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m32 = lane & 31, hh = lane >> 5;
+  const float l = pair_sum(l_run);
+  float* row = part + (size_t)(wave * 32 + m32) * kPartRow;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d = db * 32 + 8 * rg + 4 * hh;
+      *reinterpret_cast<float4*>(row + d) =
+          make_float4(o[db][4 * rg], o[db][4 * rg + 1], o[db][4 * rg + 2], o[db][4 * rg + 3]);
+    }
+  if (hh == 0) {
+    row[D] = m_run;
+    row[D + 1] = l;
+  }
+}
+
+// Merge the key-range chunks of one (query tile, head): per row, with M the
+// largest chunk max, O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c. One
+// workgroup takes 16 rows of the tile; 16 threads share a row, 8 outputs each.
+constexpr int kCombineRows = 16;
+__global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a, SegArgs seg) {
+  const int per_tile = TILE / kCombineRows;
+  const int item = blockIdx.x / per_tile;  // (qt - qt_lo) * Hq + h
+  const int r = (blockIdx.x % per_tile) * kCombineRows + (threadIdx.x >> 4);
+  const int d0 = (threadIdx.x & 15) * 8;
+  const int h = item % a.Hq;
+  const int qt = seg.qt_lo + item / a.Hq;
+  const int t = qt * TILE + r;
+  if (t >= a.S || t < seg.q_row_begin) return;
+  int lo = 0, hi = seg.n_seg - 1;  // segment of the tile
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (seg.start[mid] <= qt * TILE) lo = mid; else hi = mid - 1;
+  }
+  const int jlo = (lo == seg.n_seg - 1) ? 0 : seg.start[lo] / TILE;
+  const int nc = min(seg.chunks, (qt - jlo + seg.chunk_tiles) / seg.chunk_tiles);
+  const size_t cstride = (size_t)TILE * kPartRow;
+  const float* base = seg.part + ((size_t)item * seg.chunks * TILE + r) * kPartRow;
+  float M = -INFINITY;
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, base[c * cstride + D]);
+  float L = 0.f;
+  float acc[8] = {};
+  for (int c = 0; c < nc; ++c) {
+    const float* pc = base + c * cstride;
+    const float w = __builtin_amdgcn_exp2f(pc[D] - M);
+    L += w * pc[D + 1];
+    const float4 x0 = *reinterpret_cast<const float4*>(pc + d0);
+    const float4 x1 = *reinterpret_cast<const float4*>(pc + d0 + 4);
+    acc[0] += w * x0.x;
+    acc[1] += w * x0.y;
+    acc[2] += w * x0.z;
+    acc[3] += w * x0.w;
+    acc[4] += w * x1.x;
+    acc[5] += w * x1.y;
+    acc[6] += w * x1.z;
+    acc[7] += w * x1.w;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)t * a.Hq + h) * D + d0;
+  *reinterpret_cast<uint4*>(orow) =
+      make_uint4(cvt_pk_bf16(acc[0] * inv, acc[1] * inv), cvt_pk_bf16(acc[2] * inv, acc[3] * inv),
+                 cvt_pk_bf16(acc[4] * inv, acc[5] * inv), cvt_pk_bf16(acc[6] * inv, acc[7] * inv));
+  if (a.lse && d0 == 0)
+    a.lse[(size_t)h * a.S + t] =
+        L > 0.f ? (M + __log2f(L)) * 0.69314718055994530942f : -INFINITY;
+}
+
 // Key tiles of one unit in CSR mode: the row's block list, staged in LDS 256
 // entries at a time (a vector load inside the tile loop would make every wait
 // drain the in-flight tile DMAs); entries outside 0..qt are skipped.
@@ -253,10 +299,10 @@ struct CsrTiles {
   }
 };
 
-// Key tiles of one unit in segment mode: jlo..qt.
+// Key tiles of one unit in segment mode: jlo..jhi.
 struct SegTiles {
-  int qt;
-  __device__ int next_after(int j) const { return j < qt ? j + 1 : -1; }
+  int jhi;
+  __device__ int next_after(int j) const { return j < jhi ? j + 1 : -1; }
 };
 
 __device__ __forceinline__ int segment_of_tile(const SegArgs& s, int tile) {
@@ -277,11 +323,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
   __shared__ __attribute__((aligned(1024))) char Ks[TILE * ROWB];
   __shared__ __attribute__((aligned(1024))) char Vs[TILE * ROWB];
   __shared__ int lst[SEG ? 1 : kThreads];
-  __shared__ float2 rope[SEG ? D / 2 : 1];
   const int G = a.Hq / a.Hkv;
   const int nq = (a.S + TILE - 1) / TILE;
+  // segment mode: workgroups [0, grid_split) run key-range chunks
+  const bool chunked = SEG && (int)blockIdx.x < seg.grid_split;
   Unit u;
-  if (!decode_unit(G, a.Hkv, nq, SEG ? seg.q_row_begin / TILE : 0, u)) return;
+  if (!SEG) {
+    if (!decode_unit(blockIdx.x, G, a.Hkv, 0, nq, 1, u)) return;
+  } else if (chunked) {
+    if (!decode_unit(blockIdx.x, G, a.Hkv, seg.qt_lo, seg.qt_hi, seg.chunks, u)) return;
+  } else {
+    if (!decode_unit(blockIdx.x - seg.grid_split, G, a.Hkv, seg.rest_lo, seg.rest_hi, 1, u)) return;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m32 = lane & 31, hh = lane >> 5;
   const size_t rs = (size_t)a.Hkv * D;
@@ -298,18 +351,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
     csr.cb = csr.e;
     lst[threadIdx.x] = (csr.e + (int)threadIdx.x < csr.e1) ? col_idx[csr.e + threadIdx.x] : -1;
     lds_barrier();
-  } else {
-    const int p = segment_of_tile(seg, u.qt);
-    jseg_lo = (p == seg.n_seg - 1) ? 0 : seg.start[p] / TILE;
   }
   SegTiles segt{u.qt};
-  // Segment mode: cached keys of a segment with a nonzero offset are rotated
-  // in LDS once their tile has landed; the cos/sin table follows the offset.
-  int cur_off = 0, pj = 0;
-  auto offset_of = [&](int j) {
-    while (pj + 1 < seg.n_seg && seg.start[pj + 1] <= j * TILE) ++pj;
-    return seg.rerot[pj];
-  };
+  if (SEG) {
+    const int p = segment_of_tile(seg, u.qt);
+    jseg_lo = (p == seg.n_seg - 1) ? 0 : seg.start[p] / TILE;
+    if (chunked) {  // this workgroup's piece of the key range
+      jseg_lo += u.c * seg.chunk_tiles;
+      if (jseg_lo > u.qt) return;  // nothing left for this chunk
+      segt.jhi = min(jseg_lo + seg.chunk_tiles - 1, u.qt);
+    }
+  }
 
   bf16x8_t qf[8];
   load_q(static_cast<const uint16_t*>(a.q), a.S, a.Hq, u.h, u.qt, qf);
@@ -330,7 +382,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
   int j = SEG ? jseg_lo : csr.next(csr.e);
   wait_vmcnt<0>();  // Q fragments and the CSR chunk are in registers before any tile DMA
   if (j >= 0) {
-    if (SEG) pj = segment_of_tile(seg, j);
     dma_tile<false>(Kg, rs, a.S, j * TILE, Ks);
     dma_tile<true>(Vg, rs, a.S, j * TILE, Vs);
   }
@@ -338,23 +389,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
     const int jn = SEG ? segt.next_after(j) : csr.next(csr.e + 1);
     wait_vmcnt<8>();  // K(j) has landed (V(j) may still be in flight)
     lds_barrier();
-    if (SEG) {
-      const int off = offset_of(j);
-      if (off != 0) {
-        if (off != cur_off) {
-          if (threadIdx.x < D / 2) {
-            const double inv = pow((double)seg.theta, -2.0 * (double)threadIdx.x / (double)D);
-            double sn, cs;
-            sincos((double)off * inv, &sn, &cs);
-            rope[threadIdx.x] = make_float2((float)cs, (float)sn);
-          }
-          lds_barrier();
-          cur_off = off;
-        }
-        rotate_k_tile(Ks, rope);
-        lds_barrier();
-      }
-    }
     // ---- S^T = K Q^T (four independent accumulators in turn) ----
     // Wave priority: matrix phases win issue over the other workgroup's
     // softmax on the same SIMD (P.V highest, so a tile's output accumulation
@@ -470,17 +504,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
     if (jn >= 0) dma_tile<true>(Vg, rs, a.S, jn * TILE, Vs);
     j = jn;
   }
-  store_out(static_cast<uint16_t*>(a.out), a.lse, a.S, a.Hq, u.h, u.qt,
-            SEG ? seg.q_row_begin : 0, o, m_run, l_run);
+  if (chunked)
+    store_part(seg.part + ((((size_t)(u.qt - seg.qt_lo) * a.Hq + u.h) * seg.chunks + u.c) * TILE) *
+                              kPartRow,
+               o, m_run, l_run);
+  else
+    store_out(static_cast<uint16_t*>(a.out), a.lse, a.S, a.Hq, u.h, u.qt,
+              SEG ? seg.q_row_begin : 0, o, m_run, l_run);
 }
 
-inline int attn_grid(int Hq, int Hkv, int n_qt) {
+inline int attn_grid(int Hq, int Hkv, int n_qt, int chunks) {
   const int G = Hq / Hkv;
-  const int units = Hkv * n_qt;
-  return ((units + 7) / 8) * 8 * G;
+  const int units = Hkv * (n_qt > 0 ? n_qt : 0);
+  return ((units + 7) / 8) * 8 * G * chunks;
 }
 
 }  // namespace
+
+int attn_split_grid(int Hq, int Hkv, int n_qt, int chunks) {
+  return chunks > 0 ? attn_grid(Hq, Hkv, n_qt, chunks) : 0;
+}
 
 rbs_status launch_attn_bf16_csr(const AttnArgs& a, hipStream_t st) {
   const float scale_log2 = a.scale * 1.4426950408889634f;
@@ -489,18 +532,33 @@ rbs_status launch_attn_bf16_csr(const AttnArgs& a, hipStream_t st) {
   none.n_seg = 0;
   none.q_row_begin = 0;
   none.theta = 0.f;
-  hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3(attn_grid(a.Hq, a.Hkv, nq)), dim3(kThreads), 0,
-                     st, a, a.row_ptr, a.col_idx, none, scale_log2);
+  none.qt_lo = 0;
+  none.qt_hi = nq;
+  none.chunks = 0;
+  none.chunk_tiles = 0;
+  none.rest_lo = 0;
+  none.rest_hi = nq;
+  none.grid_split = 0;
+  none.part = nullptr;
+  hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3(attn_grid(a.Hq, a.Hkv, nq, 1)), dim3(kThreads),
+                     0, st, a, a.row_ptr, a.col_idx, none, scale_log2);
   return launch_status();
 }
 
 rbs_status launch_attn_segments(const AttnArgs& a, const SegArgs& s, hipStream_t st) {
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  const int nq = (a.S + TILE - 1) / TILE;
-  const int n_qt = nq - s.q_row_begin / TILE;
+  const int grid = s.grid_split + attn_grid(a.Hq, a.Hkv, s.rest_hi - s.rest_lo, 1);
+  if (grid == 0) return RBS_OK;
+  hipLaunchKernelGGL(attn_bf16_kernel<true>, dim3(grid), dim3(kThreads), 0, st, a, nullptr, nullptr,
+                     s, scale_log2);
+  return launch_status();
+}
+
+rbs_status launch_attn_combine(const AttnArgs& a, const SegArgs& s, hipStream_t st) {
+  const int n_qt = s.qt_hi - s.qt_lo;
   if (n_qt <= 0) return RBS_OK;
-  hipLaunchKernelGGL(attn_bf16_kernel<true>, dim3(attn_grid(a.Hq, a.Hkv, n_qt)), dim3(kThreads),
-                     0, st, a, nullptr, nullptr, s, scale_log2);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(n_qt * a.Hq * (TILE / kCombineRows)),
+                     dim3(kThreads), 0, st, a, s);
   return launch_status();
 }
 

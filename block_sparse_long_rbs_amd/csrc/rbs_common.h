@@ -85,9 +85,29 @@ struct SegArgs {
   int n_seg;
   int q_row_begin;
   float theta;
+  // One launch covers two ranges of query tiles. Workgroups [0, grid_split)
+  // take tiles [qt_lo, qt_hi), each tile's key range cut into `chunks` pieces
+  // of chunk_tiles tiles whose unnormalised partial results go to `part`
+  // (merged afterwards by the combine kernel); the remaining workgroups take
+  // tiles [rest_lo, rest_hi) whole. grid_split = 0 when nothing is split.
+  int qt_lo, qt_hi;
+  int chunks, chunk_tiles;
+  int rest_lo, rest_hi;
+  int grid_split;
+  float* part;
   int32_t start[kMaxSegments + 1];
   int32_t rerot[kMaxSegments];
 };
+// Floats per query row in the partial-result workspace: O (D), m, l, then
+// padding to a 16-byte multiple.
+constexpr int kPartRow = 128 + 4;
+// Workgroups of the split part of a segment launch (a multiple of 8).
+int attn_split_grid(int Hq, int Hkv, int n_qt, int chunks);
 rbs_status launch_attn_segments(const AttnArgs& a, const SegArgs& s, hipStream_t st);
+rbs_status launch_attn_combine(const AttnArgs& a, const SegArgs& s, hipStream_t st);
+// Position re-encoding: k_out = k_in with every key of segment p rotated by
+// s.rerot[p] positions; `table` receives n_seg * 64 cos/sin pairs.
+rbs_status launch_rerotate(const void* k_in, void* k_out, float2* table, int S, int Hkv,
+                           const SegArgs& s, hipStream_t st);
 
 }  // namespace rbs

@@ -177,15 +177,27 @@ rbs_status blocksparse_attn_fwd(rbs_dtype dt, const void* q, const void* k, cons
  *             seg_start[n_segments] = seqlen; every start except the last
  *             entry a multiple of 128.
  * k_rerotate: HOST [n_segments], >= 0.
+ * workspace:  device scratch, 256-byte aligned, caller-owned. It holds the
+ *             re-encoded keys (S x Hkv x D bf16) and their cos/sin table when
+ *             any k_rerotate[p] is nonzero, and, when the final block's rows
+ *             see many key tiles, the partial results of the chunks their key
+ *             range is cut into (merged by a second kernel). k_cached itself
+ *             is never written. workspace == NULL is a size query:
+ *             *workspace_bytes receives the bytes needed (0 when there is
+ *             nothing to re-encode or split) and nothing is enqueued.
+ *             Otherwise *workspace_bytes holds the workspace size
+ *             (RBS_E_CAPACITY if too small). Concurrent calls need separate
+ *             workspaces.
  * Supported: dt = BF16, head_dim = 128, 1 <= n_segments <= 256.
- * Errors: RBS_E_ARG, RBS_E_UNSUPPORTED, RBS_E_HIP.
+ * Errors: RBS_E_ARG, RBS_E_UNSUPPORTED, RBS_E_CAPACITY, RBS_E_HIP.
  */
 rbs_status block_mask_attn_fwd(rbs_dtype dt, const void* q, const void* k_cached,
                                const void* v, int32_t seqlen, int32_t n_q_heads,
                                int32_t n_kv_heads, int32_t head_dim, int32_t n_segments,
                                const int32_t* seg_start, const int32_t* k_rerotate,
                                float rope_theta, int32_t q_row_begin, float softmax_scale,
-                               void* out, float* lse, void* stream);
+                               void* out, float* lse, void* workspace, size_t* workspace_bytes,
+                               void* stream);
 
 #ifdef __cplusplus
 }

@@ -109,16 +109,20 @@ def test_attention_validation(L):
     assert attn(L, S=0) == E.RBS_OK
 
 
-def bmask(L, seg=(0, 128, 256, 300), rer=(0, 128, 0), **kw):
+def bmask(L, seg=(0, 128, 256, 300), rer=(0, 128, 0), ws=P, wsz=0, size_out=None, **kw):
     a = dict(dt=0, q=P, k=P, v=P, S=300, Hq=8, Hkv=2, D=128, theta=5e5, qrb=0, sc=0.0, o=P,
              lse=None)
     a.update(kw)
     n = len(seg) - 1
     ss = (ctypes.c_int32 * len(seg))(*seg)
     rr = (ctypes.c_int32 * max(1, len(rer)))(*rer)
-    return L.block_mask_attn_fwd(a["dt"], a["q"], a["k"], a["v"], a["S"], a["Hq"], a["Hkv"],
-                                 a["D"], n, ss, rr, a["theta"], a["qrb"], a["sc"], a["o"],
-                                 a["lse"], None)
+    sz = ctypes.c_size_t(wsz)
+    r = L.block_mask_attn_fwd(a["dt"], a["q"], a["k"], a["v"], a["S"], a["Hq"], a["Hkv"],
+                              a["D"], n, ss, rr, a["theta"], a["qrb"], a["sc"], a["o"],
+                              a["lse"], ws, ctypes.byref(sz), None)
+    if size_out is not None:
+        size_out.append(sz.value)
+    return r
 
 
 def test_block_mask_validation(L):
@@ -132,3 +136,32 @@ def test_block_mask_validation(L):
     assert bmask(L, dt=1) == E.RBS_E_UNSUPPORTED
     assert bmask(L, D=64) == E.RBS_E_UNSUPPORTED
     assert bmask(L, qrb=300) == E.RBS_OK                          # no rows requested
+
+
+def test_block_mask_workspace_query(L):
+    def query(**kw):
+        got = []
+        assert bmask(L, ws=None, size_out=got, **kw) == E.RBS_OK
+        return got[0]
+
+    # no offsets and a short final block: nothing to re-encode or split
+    assert query(rer=(0, 0, 0)) == 0
+    # an offset: the re-encoded keys (S * Hkv * D bf16) and the cos/sin table
+    # (n_segments * D/2 float pairs), each rounded up to 256 bytes
+    assert query() == 300 * 2 * 128 * 2 + 1536
+    # no rows requested: nothing is needed
+    assert query(qrb=300) == 0
+    # 20 passages of 1536 tokens + a 512-token final block: the final block's
+    # 4 query tiles see 241..244 key tiles and are split into 4 chunks of 64
+    seg = tuple(range(0, 30721, 1536)) + (31232,)
+    rer = tuple(range(0, 30720, 1536)) + (0,)
+    kw = dict(seg=seg, rer=rer, S=31232, Hq=32, Hkv=8)
+    keys = 31232 * 8 * 128 * 2 + 21 * 64 * 8
+    need = query(**kw)
+    assert need == keys + 4 * 32 * 4 * 128 * 132 * 4
+    # too small a workspace is refused before anything is enqueued
+    assert bmask(L, wsz=need - 1, **kw) == E.RBS_E_CAPACITY
+    # computing only the final block's last tile still splits its rows
+    assert query(qrb=31232 - 100, **kw) == keys + 1 * 32 * 4 * 128 * 132 * 4
+    # a misaligned workspace is refused
+    assert bmask(L, ws=P + 16, wsz=need, **kw) == E.RBS_E_ARG

@@ -13,13 +13,16 @@ import gpu_helpers as H
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, q_row_begin=0, tokens=None):
+def _run(w, q_row_begin=0, tokens=None, workspace=None):
     H.say(f"[case] {w.name} S={w.seqlen} segments={len(w.seg_start) - 1} q_row_begin={q_row_begin}")
     t = device.upload(w)
+    k_before = t["k"].clone()
     sentinel = torch.full_like(t["q"], 7.0)
     out, lse = rbs.block_mask_attn_fwd(t["q"], t["k"], t["v"], w.seg_start.tolist(),
                                        w.k_rerotate.tolist(), w.rope_theta,
-                                       q_row_begin=q_row_begin, want_lse=True, out=sentinel)
+                                       q_row_begin=q_row_begin, want_lse=True, out=sentinel,
+                                       workspace=workspace)
+    assert torch.equal(t["k"], k_before), "cached keys were modified"
     out_h = H.to_host(out)
     if tokens is None:
         tokens = np.arange(q_row_begin, w.seqlen)
@@ -64,3 +67,23 @@ def test_rag_31k_sampled_rows():
     final_tok = rng.choice(np.arange(int(w.seg_start[-2]), w.seqlen), size=48, replace=False)
     toks = np.sort(np.concatenate([passage_tok, final_tok, [0, w.seqlen - 1]]))
     _run(w, tokens=toks)
+
+
+def test_rag_split_final_block_all_final_rows():
+    """A final block after 132 key tiles: its rows' key ranges are split into
+    chunks run by separate workgroups and merged (every final row checked),
+    once with all rows and once with the final block only, starting inside a
+    tile."""
+    w = inputs.rag_layout(n_passages=11, passage_len=1536, final_len=300, Hq=8, Hkv=2, seed=34,
+                          name="rag_split")
+    s_last = int(w.seg_start[-2])
+    rng = np.random.default_rng(1)
+    toks = np.sort(np.concatenate([rng.choice(s_last, size=24, replace=False),
+                                   np.arange(s_last, w.seqlen)]))
+    # a workspace full of NaN bytes: nothing may depend on its prior contents
+    t = device.upload(w)
+    nbytes = rbs.block_mask_workspace_bytes(t["q"], t["k"], t["v"], w.seg_start.tolist(),
+                                            w.k_rerotate.tolist(), w.rope_theta)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    _run(w, tokens=toks, workspace=ws)
+    _run(w, q_row_begin=s_last + 37, tokens=np.arange(s_last + 37, w.seqlen), workspace=ws)
