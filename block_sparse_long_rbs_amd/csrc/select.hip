@@ -386,9 +386,9 @@ __global__ __launch_bounds__(kThreads) void select_long_kernel(SelectArgs a, int
   }
 }
 
-// CSR assembly: one workgroup per 64 rows. The row offsets are the sum of all
+// CSR assembly: one workgroup per 16 rows. The row offsets are the sum of all
 // earlier counts plus a scan inside the group; the copies are independent.
-constexpr int kCompactRows = 64;
+constexpr int kCompactRows = 16;
 
 __device__ __forceinline__ int wave_isum(int x) {
 #pragma unroll
@@ -431,12 +431,27 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(const int32_t* __rest
     if (r0 == 0 && lane == 0) row_ptr[0] = 0;
   }
   __syncthreads();
-  // copy: four threads per row
-  for (int t = tid; t < nr * 4; t += kThreads) {
-    const int rr = t >> 2, part = t & 3;
-    const int32_t* src = lists + (size_t)(r0 + rr) * stride;
-    const int c = cnt_s[rr], st = start[rr];
-    for (int e = part; e < c; e += 4) col_idx[st + e] = src[e];
+  // copy: wave w moves rows w, w + 4, w + 8, w + 12, 64 entries per pass;
+  // the four rows' loads are issued together
+  const int per = kCompactRows / 4;
+  int c[per], st[per];
+  int cmax = 0;
+#pragma unroll
+  for (int k = 0; k < per; ++k) {
+    const int rr = wave + 4 * k;
+    c[k] = rr < nr ? cnt_s[rr] : 0;
+    st[k] = rr < nr ? start[rr] : 0;
+    cmax = max(cmax, c[k]);
+  }
+  for (int e0 = 0; e0 < cmax; e0 += 64) {
+    const int e = e0 + lane;
+    int v[per];
+#pragma unroll
+    for (int k = 0; k < per; ++k)
+      v[k] = e < c[k] ? lists[(size_t)(r0 + wave + 4 * k) * stride + e] : 0;
+#pragma unroll
+    for (int k = 0; k < per; ++k)
+      if (e < c[k]) col_idx[st[k] + e] = v[k];
   }
 }
 
