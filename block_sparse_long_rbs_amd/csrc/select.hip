@@ -210,9 +210,49 @@ __device__ __forceinline__ void nth_largest_pair(const uint32_t (&ka)[M], int na
 
 constexpr int kSelM = 16;   // candidates per lane held in registers (nb <= 1024)
 
+// The n-th largest key for n <= 64 without a ballot per candidate per bit.
+// The n-th largest of the 64 per-lane maxima, T_low, is a lower bound on the
+// answer (n distinct keys are >= it), so only the keys >= T_low (n of them
+// at least, usually few more) can matter: they are compacted into `buf`
+// (this wave's LDS slice, 64 M keys) and the radix search runs on them, one
+// or a few per lane. Every key of the row >= the result is among them; a
+// result below T_low (possible only when exactly n keys are >= T_low) is
+// raised to T_low, which then has exactly n keys at or above it.
+template <int M>
+__device__ __forceinline__ uint32_t nth_largest_small(const uint32_t (&key)[M], int n,
+                                                      uint32_t* buf) {
+  const int lane = threadIdx.x & 63;
+  uint32_t lm = 0;
+#pragma unroll
+  for (int m = 0; m < M; ++m) lm = max(lm, key[m]);
+  const uint32_t lmv[1] = {lm};
+  const uint32_t tlow = nth_largest_regs<1>(lmv, n);
+  int c = 0;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const bool in = key[m] >= tlow;
+    const uint64_t msk = __ballot(in);
+    if (in) buf[c + __popcll(msk & lanemask_lt())] = key[m];
+    c += __popcll(msk);
+  }
+  uint32_t t;
+  if (c <= 64) {
+    const uint32_t k1[1] = {lane < c ? buf[lane] : 0u};
+    t = nth_largest_regs<1>(k1, n);
+  } else if (c <= 256) {
+    uint32_t k4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) k4[q] = lane + 64 * q < c ? buf[lane + 64 * q] : 0u;
+    t = nth_largest_regs<4>(k4, n);
+  } else {
+    t = nth_largest_regs<M>(key, n);
+  }
+  return max(t, tlow);
+}
+
 // One row (g, i): its i + 1 candidates, M per lane (64 M >= i + 1).
 template <int M>
-__device__ __forceinline__ void select_row(const SelectArgs& a, int g, int i) {
+__device__ __forceinline__ void select_row(const SelectArgs& a, int g, int i, uint32_t* buf) {
   const int nb = a.nb;
   const int lane = threadIdx.x & 63;
   const int nvis = i + 1;
@@ -232,7 +272,12 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, int g, int i) {
   const int nc = budget(nvis, a.rho_c);
   const int nr = budget(nvis, a.rho_r);
   uint32_t Tc, Tr;
-  nth_largest_pair(kc, nc, kr, nr, Tc, Tr);
+  if (nc <= 64 && nr <= 64) {
+    Tc = nth_largest_small(kc, nc, buf);
+    Tr = nth_largest_small(kr, nr, buf);
+  } else {
+    nth_largest_pair(kc, nc, kr, nr, Tc, Tr);
+  }
   const uint32_t bits = take_top(kc, nc, Tc) | take_top(kr, nr, Tr);
   int base = 0;
   int32_t* out = a.lists + ((size_t)g * nb + i) * a.stride;
@@ -249,6 +294,7 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, int g, int i) {
 }
 
 __global__ __launch_bounds__(kThreads) void select_rows_kernel(SelectArgs a) {
+  __shared__ uint32_t cand[kThreads / 64][64 * kSelM];
   const int nb = a.nb;
   const int wave = threadIdx.x >> 6;
   // 4 rows per workgroup, all of one KV head; heaviest rows first
@@ -256,9 +302,9 @@ __global__ __launch_bounds__(kThreads) void select_rows_kernel(SelectArgs a) {
   const int g = blockIdx.x / rows_per_g;
   const int i = nb - 1 - ((blockIdx.x % rows_per_g) * 4 + wave);
   if (i < 0) return;
-  if (i < 4 * 64) select_row<4>(a, g, i);
-  else if (i < 8 * 64) select_row<8>(a, g, i);
-  else select_row<kSelM>(a, g, i);
+  if (i < 4 * 64) select_row<4>(a, g, i, cand[wave]);
+  else if (i < 8 * 64) select_row<8>(a, g, i, cand[wave]);
+  else select_row<kSelM>(a, g, i, cand[wave]);
 }
 
 constexpr int kLongRows = 8;  // query blocks per workgroup on the long-row path

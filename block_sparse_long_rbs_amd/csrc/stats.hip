@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void block_stats_kernel(
         const T* p = qg + (size_t)to * row_stride + (size_t)vi * EPV;
         const size_t step = (size_t)TP * row_stride;
         int tt = to;
-#pragma unroll 16
+#pragma unroll 32
         for (; tt < L; tt += TP) {
           // streamed once: non-temporal loads keep Q from displacing cached data
           const u32x4_t wv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
