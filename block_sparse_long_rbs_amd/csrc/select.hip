@@ -92,7 +92,7 @@ __device__ __forceinline__ uint32_t take_top(const uint32_t (&key)[M], int n, ui
 // for j <= i form a lower triangle, cut into 64 x 64 tiles (one workgroup
 // each, equal work); every wave computes one 32 x 32 sub-tile with fp32
 // matrix-core products (v_mfma_f32_32x32x2_f32, fp32 inputs and
-// accumulation), operands read straight from L2. Scores go to a packed
+// accumulation), operands staged once per tile in LDS. Scores go to a packed
 // triangular workspace (row i starts at i (i + 1) / 2). Hkv extra workgroups
 // derive each head's rescue coefficients and store r_j * beta_j.
 // Kernel B (rows): one wave per (g, i) ranks the row's keys held in
@@ -151,13 +151,39 @@ __global__ __launch_bounds__(kThreads) void score_tiles_kernel(SelectArgs a) {
   int ti = nt - 1;
   while (t > ti) { t -= ti + 1; --ti; }
   const int tj = t;
-  const int i_base = ti * kTile + 32 * (wave >> 1);
-  const int j_base = tj * kTile + 32 * (wave & 1);
+  // the tile's 64 representative-query rows and 64 centroid rows are staged
+  // once in LDS (rows padded by 16 bytes against bank conflicts) and shared
+  // by the four waves
+  constexpr int P = D + 4;
+  constexpr int V = D / 4;                     // float4 per row
+  constexpr int NL = kTile * V / kThreads;     // float4 per thread per operand
+  __shared__ __attribute__((aligned(16))) float qs[kTile * P];
+  __shared__ __attribute__((aligned(16))) float cs[kTile * P];
+  const int i0 = ti * kTile, j0 = tj * kTile;
+  {
+    const float* qg = a.qrep + (size_t)g * nb * D;
+    const float* cg = a.cen + (size_t)g * nb * D;
+    float4 vq[NL], vc[NL];
+#pragma unroll
+    for (int n = 0; n < NL; ++n) {
+      const int x = tid + n * kThreads, r = x / V, c4 = x % V;
+      vq[n] = *reinterpret_cast<const float4*>(qg + (size_t)min(i0 + r, nb - 1) * D + 4 * c4);
+      vc[n] = *reinterpret_cast<const float4*>(cg + (size_t)min(j0 + r, nb - 1) * D + 4 * c4);
+    }
+#pragma unroll
+    for (int n = 0; n < NL; ++n) {
+      const int x = tid + n * kThreads, r = x / V, c4 = x % V;
+      *reinterpret_cast<float4*>(qs + r * P + 4 * c4) = vq[n];
+      *reinterpret_cast<float4*>(cs + r * P + 4 * c4) = vc[n];
+    }
+  }
+  __syncthreads();
+  const int i_base = i0 + 32 * (wave >> 1);
+  const int j_base = j0 + 32 * (wave & 1);
   if (j_base > i_base + 31) return;  // sub-tile entirely above the diagonal
   const int m32 = lane & 31, hh = lane >> 5;
-  const float* qrow = a.qrep + ((size_t)g * nb + min(i_base + m32, nb - 1)) * D + 4 * hh;
-  const float* crow = a.cen + ((size_t)g * nb + min(j_base + m32, nb - 1)) * D + 4 * hh;
-  // all operand loads in flight at once (the tile is latency bound)
+  const float* qrow = qs + (32 * (wave >> 1) + m32) * P + 4 * hh;
+  const float* crow = cs + (32 * (wave & 1) + m32) * P + 4 * hh;
   float4 qa[D / 8], cb[D / 8];
 #pragma unroll
   for (int s8 = 0; s8 < D / 8; ++s8) {
