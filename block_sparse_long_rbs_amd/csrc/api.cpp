@@ -173,8 +173,7 @@ rbs_status blocksparse_attn_fwd(rbs_dtype dt, const void* q, const void* k, cons
     return RBS_E_ARG;
   if (isnan(softmax_scale) || isinf(softmax_scale)) return RBS_E_ARG;
   const bool bf = dt == RBS_DT_BF16;
-  if (bf && !(head_dim == 128 && block == 128)) return RBS_E_UNSUPPORTED;
-  if (!bf && !((head_dim == 64 || head_dim == 128) && (block == 64 || block == 128)))
+  if (!((head_dim == 64 || head_dim == 128) && (block == 64 || block == 128)))
     return RBS_E_UNSUPPORTED;
   if ((int64_t)seqlen * n_q_heads * head_dim > ((int64_t)1 << 40)) return RBS_E_UNSUPPORTED;
   if (seqlen == 0) return RBS_OK;
@@ -192,7 +191,10 @@ rbs_status blocksparse_attn_fwd(rbs_dtype dt, const void* q, const void* k, cons
   a.D = head_dim;
   a.B = block;
   a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
-  return bf ? launch_attn_bf16_csr(a, as_stream(stream)) : launch_attn_f32_csr(a, as_stream(stream));
+  // bf16 at head dim 128 and block 128 runs on the matrix cores; every other
+  // supported shape on the vector-ALU kernel
+  if (bf && head_dim == 128 && block == 128) return launch_attn_bf16_csr(a, as_stream(stream));
+  return launch_attn_vec_csr(a, bf, as_stream(stream));
 }
 
 rbs_status block_mask_attn_fwd(rbs_dtype dt, const void* q, const void* k_cached,

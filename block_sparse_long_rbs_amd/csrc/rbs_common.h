@@ -76,7 +76,8 @@ struct AttnArgs {
   float scale;
 };
 rbs_status launch_attn_bf16_csr(const AttnArgs& a, hipStream_t st);
-rbs_status launch_attn_f32_csr(const AttnArgs& a, hipStream_t st);
+// Vector-ALU path: fp32 inputs, or bf16 with head dim or block 64.
+rbs_status launch_attn_vec_csr(const AttnArgs& a, bool bf16, hipStream_t st);
 int select_rows_per_group(int nb, int D);
 size_t select_score_workspace(int Hkv, int nb);
 

@@ -137,12 +137,14 @@ int64_t rbs_select_capacity(int32_t n_kv_heads, int32_t n_blocks, double keep_ra
  * the blocks listed in CSR row g * nb + i:
  *   out[t][h] = sum_u softmax_u(scale * q[t][h] . k[u][g]) v[u][g]
  *   lse[h][t] = log sum_u exp(scale * q[t][h] . k[u][g])   (natural log)
- * softmax_scale <= 0 selects 1/sqrt(head_dim). Arithmetic: bf16 inputs use
- * bf16 matrix-core products with fp32 accumulation and fp32 softmax; f32
- * inputs use fp32 throughout. out has the input dtype.
+ * softmax_scale <= 0 selects 1/sqrt(head_dim). Arithmetic: bf16 inputs at
+ * (head_dim, block) = (128, 128) use bf16 matrix-core products with fp32
+ * accumulation and fp32 softmax; every other case computes in fp32 on the
+ * vector ALUs (bf16 inputs widened exactly). out has the input dtype (a bf16
+ * out is rounded to nearest even).
  *
- * Supported (dt, head_dim, block): (BF16, 128, 128), (F32, 64, 64),
- *   (F32, 128, 64), (F32, 64, 128), (F32, 128, 128).
+ * Supported (dt, head_dim, block): dt BF16 or F32, head_dim 64 or 128,
+ *   block 64 or 128.
  * row_ptr/col_idx: device CSR as rbs_select writes it. Entries outside 0..i
  *   are skipped; a row with no usable entry gives out 0 and lse -inf.
  * lse may be NULL.

@@ -104,7 +104,8 @@ def test_attention_validation(L):
     assert attn(L, o=PM) == E.RBS_E_ARG
     assert attn(L, Hq=10, Hkv=4) == E.RBS_E_ARG
     assert attn(L, sc=float("inf")) == E.RBS_E_ARG
-    assert attn(L, D=64, B=64) == E.RBS_E_UNSUPPORTED           # bf16 supports (128, 128)
+    assert attn(L, D=96, B=128) == E.RBS_E_UNSUPPORTED           # head dim 64 or 128 only
+    assert attn(L, D=128, B=256) == E.RBS_E_UNSUPPORTED          # block 64 or 128 only
     assert attn(L, dt=1, D=96, B=64) == E.RBS_E_UNSUPPORTED
     assert attn(L, S=0) == E.RBS_OK
 

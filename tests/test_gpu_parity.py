@@ -46,6 +46,16 @@ def test_random_f32_block128():
     H.pipeline_case(w)
 
 
+@pytest.mark.parametrize("D,B", [(64, 64), (128, 64), (64, 128)])
+def test_bf16_vector_alu_shapes(D, B):
+    """bf16 at head dim or block 64 runs on the vector-ALU kernel (fp32
+    arithmetic, bf16 output); ragged tail, GQA 4:2."""
+    w = inputs.random_qkv(700, 4, 2, D, "bf16", seed=40 + D + B, block=B,
+                          name=f"bf16_vec_{D}_{B}", keep_ratio_centroid=0.3,
+                          keep_ratio_rescue=0.25, sink=True)
+    H.pipeline_case(w)
+
+
 def test_odd_gqa_ratio_bf16():
     """GQA 3:1 (odd group, single-head workgroups) with a ragged tail."""
     w = inputs.random_qkv(900, 6, 2, 128, "bf16", seed=13, block=128, name="gqa3_bf16_900",
