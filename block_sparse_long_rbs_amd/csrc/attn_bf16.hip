@@ -79,25 +79,23 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // One 16-byte-per-lane DMA from global memory (uniform base + per-lane 32-bit
-// byte offset) into LDS at lds_addr + 16*lane. Issued as inline asm so that
+// byte offset) into LDS at lds_addr + 16*lane (the LDS address goes in M0,
+// which the compiler loads for the statement). Issued as inline asm so that
 // the compiler does not treat it as a pending LDS write (it would otherwise
 // wait for every in-flight tile before each LDS read); completion is awaited
 // explicitly with wait_vmcnt.
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds_addr)
-               : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(lds_addr)
+               : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// 16-byte chunk swizzles: K rows are read 16 rows x one chunk per matrix
-// fragment, V rows 4 rows x four chunks per transposing read.
-__device__ __forceinline__ int k_swz(int row) { return row & 15; }
-__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
+// 16-byte chunk swizzles in LDS: chunk c of K row r sits at slot c ^ (r & 15)
+// (fragments read 16 rows x one chunk), chunk c of V row r at c ^ ((r & 3) << 2)
+// (transposing reads take 4 rows x four chunks).
 
 // DMA one 128 x 128 bf16 tile (tokens key0.., one KV head; src points at that
 // head's token 0) into LDS. Each of the 4 waves issues 8 loads of 1 KB (4
