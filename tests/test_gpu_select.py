@@ -40,3 +40,51 @@ def test_select_matches_oracle(nb, D, rho_c, rho_r, sink, beta_given, seed):
     H.say(f"  {diff}/{total} rows differ, all inside the threshold band")
     np.testing.assert_allclose(beta_out.cpu().numpy(), sel.beta, atol=1e-5)
     assert rp_h[-1] == len(sel.col_idx) or diff > 0
+
+
+def _patterned_stats(scores, D=64):
+    """One KV head whose centroid scores q_rep_i . c_j equal `scores[j]`
+    exactly (q_rep = e_0 with norm 1, c_j = scores[j] e_0, radius 0 so the
+    rescue branch equals the centroid branch)."""
+    nb = len(scores)
+    cen = np.zeros((1, nb, D), np.float32)
+    cen[0, :, 0] = scores
+    rad = np.zeros((1, nb), np.float32)
+    qrep = np.zeros((1, nb, D), np.float32)
+    qrep[0, :, 0] = 1.0
+    qn = np.ones((1, nb), np.float32)
+    return cen, rad, qrep, qn
+
+
+_J = np.arange(1024)
+_PATTERNS = {
+    "ascending": _J.astype(np.float32),
+    "descending": (1024 - _J).astype(np.float32),
+    "one_lane_holds_the_top": np.where(_J % 64 == 5, 1000 + _J, _J % 7).astype(np.float32),
+    "two_lanes_tied": np.where(_J % 64 < 2, 500, 1).astype(np.float32),
+    "three_values": (_J % 3).astype(np.float32),
+}
+
+
+@pytest.mark.parametrize("rho", [0.04, 0.1])
+@pytest.mark.parametrize("name", sorted(_PATTERNS))
+def test_select_exact_on_integer_scores(name, rho):
+    """Integer scores are exact in fp32 and fp64, so every row's set must equal
+    the oracle's exactly, ties going to the lower block index. The patterns
+    put the top keys in every lane, in one lane, or in long runs of ties, so
+    that the budget search meets few, some hundred, or most candidates at or
+    above its first bound (budgets up to 41 at rho 0.04, up to 103 at 0.1)."""
+    cen, rad, qrep, qn = _patterned_stats(_PATTERNS[name])
+    nb = cen.shape[1]
+    dev = lambda x: torch.from_numpy(x).cuda()
+    rp, ci, _ = rbs.rbs_select(dev(cen), dev(rad), dev(qrep), dev(qn), rho, rho, sink=False)
+    torch.cuda.synchronize()
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    ci_h = ci.cpu().numpy()[:rp_h[-1]]
+    sel = orc.select(cen.astype(np.float64), rad.astype(np.float64), qrep.astype(np.float64),
+                     qn.astype(np.float64), orc.derive_beta(rad.astype(np.float64)), rho, rho,
+                     False)
+    for i in range(nb):
+        got = ci_h[rp_h[i]:rp_h[i + 1]].tolist()
+        want = sel.col_idx[sel.row_ptr[i]:sel.row_ptr[i + 1]].tolist()
+        assert got == want, f"{name} rho={rho} row {i}: got {got} want {want}"
