@@ -18,7 +18,8 @@ Where the pages leave a step open the oracle takes one stated reading; each
 is marked READING in the function that takes it. Parity unpinned (the pages
 fix nothing, so oracle and GPU can only agree with each other): the value of
 the derived rescue coefficient beta (``derive_beta``), the pooling of the
-representative query over heads and tokens (``block_stats``), the rounding of
+representative query over heads and tokens (``block_stats``; per query head
+in ``query_rep_per_head``), the rounding of
 the per-branch budget (``budget``), the tie-break (``top_n``) and the RoPE
 pairing style (``rope_rotate``).
 
@@ -84,6 +85,26 @@ def block_stats(q: np.ndarray, k: np.ndarray, n_kv_heads: int, block: int):
         q_rep[:, b] = qb.mean(axis=(0, 2))
     q_rep_norm = np.sqrt((q_rep ** 2).sum(axis=-1))
     return centroid, radius, q_rep, q_rep_norm
+
+
+def query_rep_per_head(q: np.ndarray, block: int):
+    """Per (query head h, query block i): the mean of head h's queries over the
+    block's tokens, and its Euclidean norm.
+
+    READING (per-query-head selection): the other reading of the "q" in [RBS]
+    "The Fix" -- one representative per query head instead of one per GQA
+    group; each query head then ranks its KV head's key blocks on its own.
+    (Parity unpinned, like the group reading.)
+
+    q: [S, Hq, D]. Returns q_rep_head [Hq, nb, D], q_rep_head_norm [Hq, nb].
+    """
+    S, Hq, D = q.shape
+    nb = n_blocks(S, block)
+    rep = np.zeros((Hq, nb, D), F64)
+    for b in range(nb):
+        t0, t1 = _block_range(b, block, S)
+        rep[:, b] = q[t0:t1].astype(F64).mean(axis=0)
+    return rep, np.sqrt((rep ** 2).sum(axis=-1))
 
 
 # ---------------------------------------------------------------------------
@@ -214,6 +235,24 @@ def select(centroid, radius, q_rep, q_rep_norm, beta, keep_ratio_centroid: float
                      exempt=exempt, beta=beta)
 
 
+def select_per_head(centroid, radius, q_rep_head, q_rep_head_norm, beta,
+                    keep_ratio_centroid: float, keep_ratio_rescue: float, sink: bool,
+                    band_rel: float = 1e-4) -> Selection:
+    """Per-query-head selection: row r = h * nb + i holds query head h's blocks,
+    ranked with h's own representative query against the centroids, radii and
+    beta of its KV head g = h // G (contiguous groups), with the same branches,
+    budgets, forced blocks and ties as :func:`select`. ``beta`` is per KV head
+    [Hkv, nb]; the returned Selection keeps it that way."""
+    Hkv = centroid.shape[0]
+    Hq = q_rep_head.shape[0]
+    G = Hq // Hkv
+    per_head = lambda x: np.repeat(np.asarray(x, F64), G, axis=0)
+    sel = select(per_head(centroid), per_head(radius), q_rep_head, q_rep_head_norm,
+                 per_head(beta), keep_ratio_centroid, keep_ratio_rescue, sink, band_rel)
+    sel.beta = np.asarray(beta, F64)
+    return sel
+
+
 def select_capacity(n_kv_heads: int, nb: int, keep_ratio_centroid: float,
                     keep_ratio_rescue: float, sink: bool) -> int:
     """Largest possible number of CSR entries: per row, both budgets, the
@@ -290,6 +329,41 @@ def blocksparse_attention(q, k, v, block: int, row_ptr, col_idx, scale: Optional
         o, l = softmax_attend(logits, allowed, v[keys, g])
         out[t0:t1, g * G:(g + 1) * G] = o.transpose(1, 0, 2)
         lse[g * G:(g + 1) * G, t0:t1] = l
+    return out, lse
+
+
+def blocksparse_attention_per_head(q, k, v, block: int, row_ptr, col_idx,
+                                   scale: Optional[float] = None, rows: Optional[Iterable] = None):
+    """Causal GQA attention over per-query-head block lists: query token t in
+    block i of head h sees the tokens u <= t of the blocks in row h * nb + i
+    (keys and values of KV head h // G). Same softmax as
+    :func:`blocksparse_attention`.
+
+    rows: optional iterable of (h, i); other outputs stay NaN.
+    Returns out [S, Hq, D] and lse [Hq, S], float64.
+    """
+    S, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    nb = n_blocks(S, block)
+    scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
+    out = np.full((S, Hq, D), np.nan, F64)
+    lse = np.full((Hq, S), np.nan, F64)
+    if rows is None:
+        rows = [(h, i) for h in range(Hq) for i in range(nb)]
+    for h, i in rows:
+        g = h // G
+        r = h * nb + i
+        blocks = np.asarray(col_idx[row_ptr[r]:row_ptr[r + 1]])
+        keys = np.concatenate([np.arange(*_block_range(int(b), block, S)) for b in blocks]) \
+            if len(blocks) else np.zeros(0, np.int64)
+        t0, t1 = _block_range(i, block, S)
+        tok = np.arange(t0, t1)
+        logits = (q[t0:t1, h].astype(F64) @ k[keys, g].astype(F64).T) * scale   # [L, U]
+        allowed = keys[None, :] <= tok[:, None]
+        o, l = softmax_attend(logits[None], allowed, v[keys, g])
+        out[t0:t1, h] = o[0]
+        lse[h, t0:t1] = l[0]
     return out, lse
 
 

@@ -288,6 +288,79 @@ def test_row_zero_is_causal_attention_inside_block_zero():
     np.testing.assert_allclose(out[:64], ref, atol=1e-12, rtol=0)
 
 
+# ---------------------------------------------------------------- per-query-head selection
+
+def test_per_head_reps_average_to_the_group_rep():
+    """The mean of a group's per-head representatives is the group's (equal
+    token counts per head), ragged last block included."""
+    w = inputs.random_qkv(300, 6, 2, 16, "f32", seed=12, block=64)
+    _, _, qr, _ = orc.block_stats(w.q, w.k, 2, 64)
+    qh, qhn = orc.query_rep_per_head(w.q, 64)
+    np.testing.assert_allclose(qh.reshape(2, 3, -1, 16).mean(axis=1), qr, atol=1e-13, rtol=0)
+    np.testing.assert_allclose(qhn, np.linalg.norm(qh, axis=-1), atol=1e-13, rtol=0)
+
+
+def _identical_heads(w, G):
+    q = w.q.copy()
+    for h in range(q.shape[1]):
+        q[:, h] = w.q[:, (h // G) * G]
+    return q
+
+
+def test_per_head_selection_with_identical_heads_is_the_group_selection():
+    w = inputs.mixture_small(S=640, Hq=8, Hkv=2, D=32, B=64, rho=0.2, sink=True, seed=6)
+    q = _identical_heads(w, 4)
+    c, r, qr, qn = orc.block_stats(q, w.k, 2, 64)
+    beta = orc.derive_beta(r)
+    grp = orc.select(c, r, qr, qn, beta, 0.2, 0.15, sink=True)
+    qh, qhn = orc.query_rep_per_head(q, 64)
+    per = orc.select_per_head(c, r, qh, qhn, beta, 0.2, 0.15, sink=True)
+    nb = w.n_blocks
+    for h in range(8):
+        for i in range(nb):
+            assert per.col_idx[per.row_ptr[h * nb + i]:per.row_ptr[h * nb + i + 1]].tolist() == \
+                grp.row(h // 4, i).tolist()
+
+
+def test_planted_tiled_head_mapping_breaks_identical_heads_pin():
+    """Pairing query head h with KV head h % Hkv (tiling instead of repeating
+    the KV-head statistics) gives other rows, so the pin above catches it."""
+    w = inputs.mixture_small(S=640, Hq=8, Hkv=2, D=32, B=64, rho=0.2, sink=True, seed=6)
+    q = _identical_heads(w, 4)
+    c, r, qr, qn = orc.block_stats(q, w.k, 2, 64)
+    beta = orc.derive_beta(r)
+    grp = orc.select(c, r, qr, qn, beta, 0.2, 0.15, sink=True)
+    qh, qhn = orc.query_rep_per_head(q, 64)
+    tiled = orc.select(np.tile(c, (4, 1, 1)), np.tile(r, (4, 1)), qh, qhn, np.tile(beta, (4, 1)),
+                       0.2, 0.15, sink=True)
+    nb = w.n_blocks
+    assert any(tiled.col_idx[tiled.row_ptr[h * nb + i]:tiled.row_ptr[h * nb + i + 1]].tolist()
+               != grp.row(h // 4, i).tolist() for h in range(8) for i in range(nb))
+
+
+def test_per_head_attention_equals_token_level_brute_force():
+    w = inputs.mixture_small(S=200, Hq=4, Hkv=2, D=16, B=32, rho=0.3, sink=False, seed=4)
+    c, r, _, _ = orc.block_stats(w.q, w.k, 2, 32)
+    qh, qhn = orc.query_rep_per_head(w.q, 32)
+    sel = orc.select_per_head(c, r, qh, qhn, orc.derive_beta(r), 0.3, 0.3, sink=False)
+    out, lse = orc.blocksparse_attention_per_head(w.q, w.k, w.v, 32, sel.row_ptr, sel.col_idx)
+    mask = orc.csr_token_mask(sel.row_ptr, sel.col_idx, 4, 200, 32)   # one mask per query head
+    for h in range(4):
+        g = h // 2
+        o2, l2 = orc.masked_attention(w.q[:, h:h + 1], w.k[:, g:g + 1], w.v[:, g:g + 1], mask[h])
+        np.testing.assert_allclose(out[:, h], o2[:, 0], atol=1e-12, rtol=0)
+        np.testing.assert_allclose(lse[h], l2[0], atol=1e-12, rtol=0)
+
+
+def test_per_head_keep_ratio_one_is_dense_causal_attention():
+    w = inputs.random_qkv(300, 4, 2, 32, "f32", seed=9, block=64)
+    c, r, _, _ = orc.block_stats(w.q, w.k, 2, 64)
+    qh, qhn = orc.query_rep_per_head(w.q, 64)
+    sel = orc.select_per_head(c, r, qh, qhn, orc.derive_beta(r), 1.0, 1.0, sink=False)
+    out, _ = orc.blocksparse_attention_per_head(w.q, w.k, w.v, 64, sel.row_ptr, sel.col_idx)
+    np.testing.assert_allclose(out, _sdpa_causal(w.q, w.k, w.v), atol=1e-12, rtol=0)
+
+
 # ---------------------------------------------------------------- Block-attention
 
 def test_rope_composition():
