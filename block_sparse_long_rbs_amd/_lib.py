@@ -35,6 +35,14 @@ _SIGS = {
                                   _c_u32, _vp, _vp, _vp, _c_i64, _vp,
                                   ctypes.POINTER(ctypes.c_size_t), _vp]),
     "rbs_select_capacity": (_c_i64, [_c_i32, _c_i32, _c_f64, _c_f64, _c_u32]),
+    "rbs_block_stats_per_head": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _c_i32, _c_i32, _c_i32,
+                                                _c_i32, _c_i32, _vp, _vp, _vp, _vp, _vp]),
+    "rbs_select_per_head": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
+                                           _c_f64, _c_f64, _c_u32, _vp, _vp, _vp, _c_i64, _vp,
+                                           ctypes.POINTER(ctypes.c_size_t), _vp]),
+    "blocksparse_attn_fwd_per_head": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _c_i32, _c_i32,
+                                                     _c_i32, _c_i32, _c_i32, _vp, _vp, _c_f32,
+                                                     _vp, _vp, _vp]),
     "blocksparse_attn_fwd": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
                                             _c_i32, _c_i32, _vp, _vp, _c_f32, _vp, _vp, _vp]),
     "block_mask_attn_fwd": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
@@ -125,6 +133,23 @@ def rbs_block_stats(q: torch.Tensor, k: torch.Tensor, block: int):
     return cen, rad, qrep, qn
 
 
+def rbs_block_stats_per_head(q: torch.Tensor, k: torch.Tensor, block: int):
+    """Centroid and radius per KV head, representative query per query head:
+    -> fp32 (cen [Hkv,nb,D], rad [Hkv,nb], q_rep_head [Hq,nb,D],
+    q_rep_head_norm [Hq,nb])."""
+    _need_cuda(q, k)
+    S, Hq, D = q.shape
+    Hkv = k.shape[1]
+    nb = -(-S // block)
+    f = dict(device=q.device, dtype=torch.float32)
+    cen, qrep = torch.empty((Hkv, nb, D), **f), torch.empty((Hq, nb, D), **f)
+    rad, qn = torch.empty((Hkv, nb), **f), torch.empty((Hq, nb), **f)
+    _check("rbs_block_stats_per_head", lib().rbs_block_stats_per_head(
+        _dtype_code(q), q.data_ptr(), k.data_ptr(), S, Hq, Hkv, D, block, cen.data_ptr(),
+        rad.data_ptr(), qrep.data_ptr(), qn.data_ptr(), _stream(q)))
+    return cen, rad, qrep, qn
+
+
 def rbs_select_capacity(n_kv_heads: int, n_blocks: int, keep_ratio_centroid: float,
                         keep_ratio_rescue: float, sink: bool = False) -> int:
     return int(lib().rbs_select_capacity(n_kv_heads, n_blocks, keep_ratio_centroid,
@@ -157,6 +182,53 @@ def rbs_select(cen, rad, qrep, qnorm, keep_ratio_centroid: float, keep_ratio_res
         keep_ratio_centroid, keep_ratio_rescue, flags, _ptr(beta_out), row_ptr.data_ptr(),
         col_idx.data_ptr(), cap, workspace.data_ptr(), ctypes.byref(wsz), _stream(cen)))
     return row_ptr, col_idx, beta_out
+
+
+def rbs_select_per_head(cen, rad, qrep_head, qnorm_head, keep_ratio_centroid: float,
+                        keep_ratio_rescue: float, sink: bool = False,
+                        beta: Optional[torch.Tensor] = None, want_beta: bool = False,
+                        workspace: Optional[torch.Tensor] = None):
+    """Per-query-head selection -> (row_ptr [Hq*nb+1] int32, col_idx int32,
+    beta_used [Hkv,nb] fp32 or None); rows h * nb + i."""
+    _need_cuda(cen, rad, qrep_head, qnorm_head, beta)
+    Hkv, nb, D = cen.shape
+    Hq = qrep_head.shape[0]
+    flags = RBS_SEL_FORCE_SINK if sink else 0
+    L = lib()
+    ws = ctypes.c_size_t(0)
+    _check("rbs_select_per_head", L.rbs_select_per_head(
+        None, None, None, None, None, Hq, Hkv, nb, D, keep_ratio_centroid, keep_ratio_rescue,
+        flags, None, None, None, 0, None, ctypes.byref(ws), None))
+    if workspace is None or workspace.numel() < ws.value:
+        workspace = torch.empty(ws.value, dtype=torch.uint8, device=cen.device)
+    cap = rbs_select_capacity(Hq, nb, keep_ratio_centroid, keep_ratio_rescue, sink)
+    row_ptr = torch.empty(Hq * nb + 1, dtype=torch.int32, device=cen.device)
+    col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=cen.device)
+    beta_out = torch.empty((Hkv, nb), dtype=torch.float32, device=cen.device) if want_beta else None
+    wsz = ctypes.c_size_t(workspace.numel())
+    _check("rbs_select_per_head", L.rbs_select_per_head(
+        cen.data_ptr(), rad.data_ptr(), qrep_head.data_ptr(), qnorm_head.data_ptr(), _ptr(beta),
+        Hq, Hkv, nb, D, keep_ratio_centroid, keep_ratio_rescue, flags, _ptr(beta_out),
+        row_ptr.data_ptr(), col_idx.data_ptr(), cap, workspace.data_ptr(), ctypes.byref(wsz),
+        _stream(cen)))
+    return row_ptr, col_idx, beta_out
+
+
+def blocksparse_attn_fwd_per_head(q, k, v, block: int, row_ptr, col_idx,
+                                  softmax_scale: float = 0.0, want_lse: bool = False,
+                                  out: Optional[torch.Tensor] = None):
+    """Causal GQA attention over per-query-head CSR block lists (row h * nb + i)."""
+    _need_cuda(q, k, v, row_ptr, col_idx)
+    S, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((Hq, S), dtype=torch.float32, device=q.device) if want_lse else None
+    _check("blocksparse_attn_fwd_per_head", lib().blocksparse_attn_fwd_per_head(
+        _dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), S, Hq, Hkv, D, block,
+        row_ptr.data_ptr(), col_idx.data_ptr(), softmax_scale, out.data_ptr(), _ptr(lse),
+        _stream(q)))
+    return out, lse
 
 
 def blocksparse_attn_fwd(q, k, v, block: int, row_ptr, col_idx, softmax_scale: float = 0.0,

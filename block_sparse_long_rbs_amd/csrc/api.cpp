@@ -52,64 +52,53 @@ namespace {
 constexpr int kChunkTiles = 64;
 }  // namespace
 
-extern "C" {
-
-const char* rbs_status_string(rbs_status s) {
-  switch (s) {
-    case RBS_OK: return "ok";
-    case RBS_E_ARG: return "invalid argument";
-    case RBS_E_UNSUPPORTED: return "unsupported configuration";
-    case RBS_E_CAPACITY: return "output capacity or workspace too small";
-    case RBS_E_HIP: return "HIP runtime error";
-  }
-  return "unknown status";
-}
-
-rbs_status rbs_block_stats(rbs_dtype dt, const void* q, const void* k, int32_t seqlen,
-                           int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block,
-                           float* k_centroid, float* k_radius, float* q_rep, float* q_rep_norm,
-                           void* stream) {
+namespace {
+rbs_status block_stats_common(rbs_dtype dt, const void* q, const void* k, int32_t seqlen,
+                              int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                              int32_t block, float* k_centroid, float* k_radius, float* q_rep,
+                              float* q_rep_norm, float* q_rep_head, float* q_rep_head_norm,
+                              void* stream) {
   if (dt != RBS_DT_BF16 && dt != RBS_DT_F32) return RBS_E_ARG;
   if (seqlen < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || block <= 0)
     return RBS_E_ARG;
   if (n_q_heads % n_kv_heads != 0) return RBS_E_ARG;
   if (seqlen > 0 && (!aligned(q, 16) || !aligned(k, 16) || !aligned(k_centroid, 16) ||
-                     !aligned(q_rep, 16) || !aligned(k_radius, 4) || !aligned(q_rep_norm, 4)))
+                     !aligned(k_radius, 4)))
+    return RBS_E_ARG;
+  if (seqlen > 0 && q_rep && (!aligned(q_rep, 16) || !aligned(q_rep_norm, 4))) return RBS_E_ARG;
+  if (seqlen > 0 && q_rep_head && (!aligned(q_rep_head, 16) || !aligned(q_rep_head_norm, 4)))
     return RBS_E_ARG;
   if (head_dim != 64 && head_dim != 128) return RBS_E_UNSUPPORTED;
   if (block < 16 || block > 256 || block % 16 != 0) return RBS_E_UNSUPPORTED;
   // LDS of the stats kernel grows with the group's row width
   const int esize = dt == RBS_DT_BF16 ? 2 : 4;
   const int epv = 16 / esize;
-  const int vr = (n_q_heads / n_kv_heads) * (head_dim / epv);
+  const int G = n_q_heads / n_kv_heads;
+  const int vr = G * (head_dim / epv);
   const size_t qslots = vr <= 256 ? (size_t)(256 / vr) * vr : (size_t)vr;
-  if ((qslots * epv + 16 + 256 * epv + head_dim) * 4 > 64 * 1024) return RBS_E_UNSUPPORTED;
+  if ((qslots * epv + 16 + 256 * epv + head_dim + (size_t)G * (head_dim / 64)) * 4 > 64 * 1024)
+    return RBS_E_UNSUPPORTED;
   if ((int64_t)seqlen * n_q_heads * head_dim > ((int64_t)1 << 40)) return RBS_E_UNSUPPORTED;
   if (seqlen == 0) return RBS_OK;
   return launch_block_stats(dt, q, k, seqlen, n_q_heads, n_kv_heads, head_dim, block, k_centroid,
-                            k_radius, q_rep, q_rep_norm, as_stream(stream));
+                            k_radius, q_rep, q_rep_norm, q_rep_head, q_rep_head_norm,
+                            as_stream(stream));
 }
+}  // namespace
 
-int64_t rbs_select_capacity(int32_t n_kv_heads, int32_t n_blocks, double keep_ratio_centroid,
-                            double keep_ratio_rescue, uint32_t flags) {
-  if (n_kv_heads <= 0 || n_blocks < 0 || !ratio_ok(keep_ratio_centroid) ||
-      !ratio_ok(keep_ratio_rescue))
-    return -1;
-  int64_t total;
-  int widest;
-  select_sizes(n_blocks, keep_ratio_centroid, keep_ratio_rescue, (flags & RBS_SEL_FORCE_SINK) != 0,
-               &total, &widest);
-  return total * n_kv_heads;
-}
-
-rbs_status rbs_select(const float* k_centroid, const float* k_radius, const float* q_rep,
-                      const float* q_rep_norm, const float* beta_in, int32_t n_kv_heads,
-                      int32_t n_blocks, int32_t head_dim, double keep_ratio_centroid,
-                      double keep_ratio_rescue, uint32_t flags, float* beta_out,
-                      int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
-                      void* workspace, size_t* workspace_bytes, void* stream) {
+namespace {
+// One list per row head: n_row_heads = n_kv_heads (a list per GQA group) or
+// n_q_heads (a list per query head); q_rep / q_rep_norm are per row head.
+rbs_status select_common(const float* k_centroid, const float* k_radius, const float* q_rep,
+                         const float* q_rep_norm, const float* beta_in, int32_t n_row_heads,
+                         int32_t n_kv_heads, int32_t n_blocks, int32_t head_dim,
+                         double keep_ratio_centroid, double keep_ratio_rescue, uint32_t flags,
+                         float* beta_out, int32_t* row_ptr, int32_t* col_idx,
+                         int64_t col_capacity, void* workspace, size_t* workspace_bytes,
+                         void* stream) {
   if (!workspace_bytes) return RBS_E_ARG;
-  if (n_kv_heads <= 0 || n_blocks < 0 || head_dim <= 0) return RBS_E_ARG;
+  if (n_kv_heads <= 0 || n_row_heads <= 0 || n_row_heads % n_kv_heads != 0) return RBS_E_ARG;
+  if (n_blocks < 0 || head_dim <= 0) return RBS_E_ARG;
   if (!ratio_ok(keep_ratio_centroid) || !ratio_ok(keep_ratio_rescue)) return RBS_E_ARG;
   if ((flags & ~RBS_SEL_FORCE_SINK) != 0) return RBS_E_ARG;
   if (head_dim != 64 && head_dim != 128) return RBS_E_UNSUPPORTED;
@@ -118,10 +107,10 @@ rbs_status rbs_select(const float* k_centroid, const float* k_radius, const floa
   int64_t per_head;
   int widest;
   select_sizes(n_blocks, keep_ratio_centroid, keep_ratio_rescue, sink, &per_head, &widest);
-  const int64_t rows = (int64_t)n_kv_heads * n_blocks;
+  const int64_t rows = (int64_t)n_row_heads * n_blocks;
   const size_t counts_bytes = align256((size_t)rows * 4);
   const size_t lists_bytes = align256((size_t)rows * widest * 4);
-  const size_t scores_bytes = align256(select_score_workspace(n_kv_heads, n_blocks));
+  const size_t scores_bytes = align256(select_score_workspace(n_row_heads, n_blocks));
   const size_t need = 256 + counts_bytes + lists_bytes + scores_bytes;
   if (!workspace) {
     *workspace_bytes = need;
@@ -133,8 +122,8 @@ rbs_status rbs_select(const float* k_centroid, const float* k_radius, const floa
     return RBS_E_ARG;
   if ((beta_in && !aligned(beta_in, 4)) || (beta_out && !aligned(beta_out, 4))) return RBS_E_ARG;
   if (*workspace_bytes < need) return RBS_E_CAPACITY;
-  if (col_capacity < per_head * n_kv_heads) return RBS_E_CAPACITY;
-  if (per_head * n_kv_heads > INT32_MAX) return RBS_E_UNSUPPORTED;
+  if (col_capacity < per_head * n_row_heads) return RBS_E_CAPACITY;
+  if (per_head * n_row_heads > INT32_MAX) return RBS_E_UNSUPPORTED;
   SelectArgs a;
   a.cen = k_centroid;
   a.rad = k_radius;
@@ -148,8 +137,9 @@ rbs_status rbs_select(const float* k_centroid, const float* k_radius, const floa
   a.lists = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 256 + counts_bytes);
   a.scores = reinterpret_cast<float*>(static_cast<char*>(workspace) + 256 + counts_bytes +
                                       lists_bytes);
-  a.rbeta = a.scores + (size_t)n_kv_heads * ((size_t)n_blocks * (n_blocks + 1) / 2);
-  a.Hkv = n_kv_heads;
+  a.rbeta = a.scores + (size_t)n_row_heads * ((size_t)n_blocks * (n_blocks + 1) / 2);
+  a.H = n_row_heads;
+  a.G = n_row_heads / n_kv_heads;
   a.nb = n_blocks;
   a.D = head_dim;
   a.stride = widest;
@@ -159,11 +149,13 @@ rbs_status rbs_select(const float* k_centroid, const float* k_radius, const floa
   return launch_select(a, as_stream(stream));
 }
 
-rbs_status blocksparse_attn_fwd(rbs_dtype dt, const void* q, const void* k, const void* v,
-                                int32_t seqlen, int32_t n_q_heads, int32_t n_kv_heads,
-                                int32_t head_dim, int32_t block, const int32_t* row_ptr,
-                                const int32_t* col_idx, float softmax_scale, void* out,
-                                float* lse, void* stream) {
+}  // namespace
+
+namespace {
+rbs_status attn_common(rbs_dtype dt, const void* q, const void* k, const void* v, int32_t seqlen,
+                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block,
+                       const int32_t* row_ptr, const int32_t* col_idx, float softmax_scale,
+                       void* out, float* lse, bool per_head, void* stream) {
   if (dt != RBS_DT_BF16 && dt != RBS_DT_F32) return RBS_E_ARG;
   if (seqlen < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || block <= 0)
     return RBS_E_ARG;
@@ -191,10 +183,99 @@ rbs_status blocksparse_attn_fwd(rbs_dtype dt, const void* q, const void* k, cons
   a.D = head_dim;
   a.B = block;
   a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
+  a.per_head = per_head ? 1 : 0;
   // bf16 at head dim 128 and block 128 runs on the matrix cores; every other
   // supported shape on the vector-ALU kernel
   if (bf && head_dim == 128 && block == 128) return launch_attn_bf16_csr(a, as_stream(stream));
   return launch_attn_vec_csr(a, bf, as_stream(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rbs_status_string(rbs_status s) {
+  switch (s) {
+    case RBS_OK: return "ok";
+    case RBS_E_ARG: return "invalid argument";
+    case RBS_E_UNSUPPORTED: return "unsupported configuration";
+    case RBS_E_CAPACITY: return "output capacity or workspace too small";
+    case RBS_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+rbs_status rbs_block_stats(rbs_dtype dt, const void* q, const void* k, int32_t seqlen,
+                           int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block,
+                           float* k_centroid, float* k_radius, float* q_rep, float* q_rep_norm,
+                           void* stream) {
+  if (seqlen > 0 && (!q_rep || !q_rep_norm)) return RBS_E_ARG;
+  return block_stats_common(dt, q, k, seqlen, n_q_heads, n_kv_heads, head_dim, block, k_centroid,
+                            k_radius, q_rep, q_rep_norm, nullptr, nullptr, stream);
+}
+
+rbs_status rbs_block_stats_per_head(rbs_dtype dt, const void* q, const void* k, int32_t seqlen,
+                                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                    int32_t block, float* k_centroid, float* k_radius,
+                                    float* q_rep_head, float* q_rep_head_norm, void* stream) {
+  if (seqlen > 0 && (!q_rep_head || !q_rep_head_norm)) return RBS_E_ARG;
+  return block_stats_common(dt, q, k, seqlen, n_q_heads, n_kv_heads, head_dim, block, k_centroid,
+                            k_radius, nullptr, nullptr, q_rep_head, q_rep_head_norm, stream);
+}
+
+int64_t rbs_select_capacity(int32_t n_kv_heads, int32_t n_blocks, double keep_ratio_centroid,
+                            double keep_ratio_rescue, uint32_t flags) {
+  if (n_kv_heads <= 0 || n_blocks < 0 || !ratio_ok(keep_ratio_centroid) ||
+      !ratio_ok(keep_ratio_rescue))
+    return -1;
+  int64_t total;
+  int widest;
+  select_sizes(n_blocks, keep_ratio_centroid, keep_ratio_rescue, (flags & RBS_SEL_FORCE_SINK) != 0,
+               &total, &widest);
+  return total * n_kv_heads;
+}
+
+rbs_status rbs_select(const float* k_centroid, const float* k_radius, const float* q_rep,
+                      const float* q_rep_norm, const float* beta_in, int32_t n_kv_heads,
+                      int32_t n_blocks, int32_t head_dim, double keep_ratio_centroid,
+                      double keep_ratio_rescue, uint32_t flags, float* beta_out,
+                      int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                      void* workspace, size_t* workspace_bytes, void* stream) {
+  return select_common(k_centroid, k_radius, q_rep, q_rep_norm, beta_in, n_kv_heads, n_kv_heads,
+                       n_blocks, head_dim, keep_ratio_centroid, keep_ratio_rescue, flags, beta_out,
+                       row_ptr, col_idx, col_capacity, workspace, workspace_bytes, stream);
+}
+
+rbs_status rbs_select_per_head(const float* k_centroid, const float* k_radius,
+                               const float* q_rep_head, const float* q_rep_head_norm,
+                               const float* beta_in, int32_t n_q_heads, int32_t n_kv_heads,
+                               int32_t n_blocks, int32_t head_dim, double keep_ratio_centroid,
+                               double keep_ratio_rescue, uint32_t flags, float* beta_out,
+                               int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                               void* workspace, size_t* workspace_bytes, void* stream) {
+  return select_common(k_centroid, k_radius, q_rep_head, q_rep_head_norm, beta_in, n_q_heads,
+                       n_kv_heads, n_blocks, head_dim, keep_ratio_centroid, keep_ratio_rescue,
+                       flags, beta_out, row_ptr, col_idx, col_capacity, workspace,
+                       workspace_bytes, stream);
+}
+
+rbs_status blocksparse_attn_fwd(rbs_dtype dt, const void* q, const void* k, const void* v,
+                                int32_t seqlen, int32_t n_q_heads, int32_t n_kv_heads,
+                                int32_t head_dim, int32_t block, const int32_t* row_ptr,
+                                const int32_t* col_idx, float softmax_scale, void* out,
+                                float* lse, void* stream) {
+  return attn_common(dt, q, k, v, seqlen, n_q_heads, n_kv_heads, head_dim, block, row_ptr,
+                     col_idx, softmax_scale, out, lse, false, stream);
+}
+
+rbs_status blocksparse_attn_fwd_per_head(rbs_dtype dt, const void* q, const void* k,
+                                         const void* v, int32_t seqlen, int32_t n_q_heads,
+                                         int32_t n_kv_heads, int32_t head_dim, int32_t block,
+                                         const int32_t* row_ptr, const int32_t* col_idx,
+                                         float softmax_scale, void* out, float* lse,
+                                         void* stream) {
+  return attn_common(dt, q, k, v, seqlen, n_q_heads, n_kv_heads, head_dim, block, row_ptr,
+                     col_idx, softmax_scale, out, lse, true, stream);
 }
 
 rbs_status block_mask_attn_fwd(rbs_dtype dt, const void* q, const void* k_cached,
@@ -264,6 +345,7 @@ rbs_status block_mask_attn_fwd(rbs_dtype dt, const void* q, const void* k_cached
   a.lse = lse;
   a.row_ptr = nullptr;
   a.col_idx = nullptr;
+  a.per_head = 0;
   a.S = seqlen;
   a.Hq = n_q_heads;
   a.Hkv = n_kv_heads;

@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
   CsrTiles csr{col_idx, 0, 0, 0, u.qt, lst};
   int jseg_lo = 0;
   if (!SEG) {
-    const int row = u.g * nq + u.qt;
+    const int row = (a.per_head ? u.h : u.g) * nq + u.qt;
     csr.e = row_ptr[row];
     csr.e1 = row_ptr[row + 1];
     csr.cb = csr.e;

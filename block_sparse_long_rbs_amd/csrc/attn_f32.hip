@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnArgs a) {
     o[d] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
-  const int row = g * nb + i;
+  const int row = (a.per_head ? h : g) * nb + i;
   const int e0 = a.row_ptr[row], e1 = a.row_ptr[row + 1];
   for (int e = e0; e < e1; ++e) {
     const int j = a.col_idx[e];

@@ -41,9 +41,11 @@ inline rbs_status launch_status() {
 }
 
 // Host launchers (one per kernel family); arguments are validated by the API layer.
+// qrep/qnorm (per KV head) and qrep_h/qnorm_h (per query head) may each be
+// null; the other outputs are always written.
 rbs_status launch_block_stats(rbs_dtype dt, const void* q, const void* k, int S, int Hq, int Hkv,
                               int D, int B, float* cen, float* rad, float* qrep, float* qnorm,
-                              hipStream_t st);
+                              float* qrep_h, float* qnorm_h, hipStream_t st);
 
 struct SelectArgs {
   const float* cen;
@@ -54,11 +56,15 @@ struct SelectArgs {
   float* beta_out;
   int32_t* row_ptr;
   int32_t* col_idx;
-  int32_t* counts;   // workspace: [Hkv*nb]
-  int32_t* lists;    // workspace: [Hkv*nb][stride]
-  float* scores;     // workspace: packed triangular centroid scores (nb <= 1024)
-  float* rbeta;      // workspace: r_j * beta_j per head (nb <= 1024)
-  int Hkv, nb, D, stride;
+  int32_t* counts;   // workspace: [H*nb]
+  int32_t* lists;    // workspace: [H*nb][stride]
+  float* scores;     // workspace: packed triangular centroid scores per row head (nb <= 1024)
+  float* rbeta;      // workspace: r_j * beta_j per KV head (nb <= 1024)
+  // Rows r = h * nb + i for h < H row heads: H = n_kv_heads with G = 1 (one
+  // list per GQA group), or H = n_q_heads with G = n_q_heads / n_kv_heads (one
+  // list per query head). qrep/qnorm are per row head; cen, rad and beta per
+  // KV head h / G.
+  int H, G, nb, D, stride;
   double rho_c, rho_r;
   int sink;
 };
@@ -74,12 +80,13 @@ struct AttnArgs {
   const int32_t* col_idx;
   int S, Hq, Hkv, D, B;
   float scale;
+  int per_head;   // CSR rows per query head (h * nb + i) instead of per KV head (g * nb + i)
 };
 rbs_status launch_attn_bf16_csr(const AttnArgs& a, hipStream_t st);
 // Vector-ALU path: fp32 inputs, or bf16 with head dim or block 64.
 rbs_status launch_attn_vec_csr(const AttnArgs& a, bool bf16, hipStream_t st);
 int select_rows_per_group(int nb, int D);
-size_t select_score_workspace(int Hkv, int nb);
+size_t select_score_workspace(int H, int nb);
 
 constexpr int kMaxSegments = 256;
 struct SegArgs {

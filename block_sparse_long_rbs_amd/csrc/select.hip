@@ -93,8 +93,8 @@ __device__ __forceinline__ uint32_t take_top(const uint32_t (&key)[M], int n, ui
 // each, equal work); every wave computes one 32 x 32 sub-tile with fp32
 // matrix-core products (v_mfma_f32_32x32x2_f32, fp32 inputs and
 // accumulation), operands staged once per tile in LDS. Scores go to a packed
-// triangular workspace (row i starts at i (i + 1) / 2). Hkv extra workgroups
-// derive each head's rescue coefficients and store r_j * beta_j.
+// triangular workspace (row i starts at i (i + 1) / 2). One extra workgroup
+// per KV head derives its rescue coefficients and stores r_j * beta_j.
 // Kernel B (rows): one wave per (g, i) ranks the row's keys held in
 // registers (centroid key and rescue key per candidate) and writes the
 // selected block list.
@@ -108,21 +108,24 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void score_tiles_kernel(SelectArgs a) {
-  const int g = blockIdx.y;
+  const int g = blockIdx.y;       // row head
+  const int gk = g / a.G;          // its KV head
   const int nb = a.nb;
   const int nt = (nb + kTile - 1) / kTile;
   const int ntiles = nt * (nt + 1) / 2;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if ((int)blockIdx.x >= ntiles) {
-    // rescue coefficients of head g: beta = clamp((r - mean) / (max - mean), 0, 1)
+    // rescue coefficients of KV head gk (once, from its first row head):
+    // beta = clamp((r - mean) / (max - mean), 0, 1)
     __shared__ float red[8];
-    const float* rad = a.rad + (size_t)g * nb;
-    float* rb = a.rbeta + (size_t)g * nb;
+    if (g % a.G != 0) return;
+    const float* rad = a.rad + (size_t)gk * nb;
+    float* rb = a.rbeta + (size_t)gk * nb;
     if (a.beta_in) {
-      const float* bi = a.beta_in + (size_t)g * nb;
+      const float* bi = a.beta_in + (size_t)gk * nb;
       for (int j = tid; j < nb; j += kThreads) {
         rb[j] = rad[j] * bi[j];
-        if (a.beta_out) a.beta_out[(size_t)g * nb + j] = bi[j];
+        if (a.beta_out) a.beta_out[(size_t)gk * nb + j] = bi[j];
       }
       return;
     }
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void score_tiles_kernel(SelectArgs a) {
     for (int j = tid; j < nb; j += kThreads) {
       const float b = ok ? fminf(fmaxf((rad[j] - mean) / spread, 0.f), 1.f) : 0.f;
       rb[j] = rad[j] * b;
-      if (a.beta_out) a.beta_out[(size_t)g * nb + j] = b;
+      if (a.beta_out) a.beta_out[(size_t)gk * nb + j] = b;
     }
     return;
   }
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void score_tiles_kernel(SelectArgs a) {
   const int i0 = ti * kTile, j0 = tj * kTile;
   {
     const float* qg = a.qrep + (size_t)g * nb * D;
-    const float* cg = a.cen + (size_t)g * nb * D;
+    const float* cg = a.cen + (size_t)gk * nb * D;
     float4 vq[NL], vc[NL];
 #pragma unroll
     for (int n = 0; n < NL; ++n) {
@@ -284,7 +287,7 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, int g, int i, ui
   const int nvis = i + 1;
   const float qn = a.qnorm[(size_t)g * nb + i];
   const float* srow = a.scores + (size_t)g * tri_off(nb) + tri_off(i);
-  const float* rb = a.rbeta + (size_t)g * nb;
+  const float* rb = a.rbeta + (size_t)(g / a.G) * nb;
   uint32_t kc[M], kr[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) {
@@ -335,6 +338,9 @@ __global__ __launch_bounds__(kThreads) void select_rows_kernel(SelectArgs a) {
 
 constexpr int kLongRows = 8;  // query blocks per workgroup on the long-row path
 
+// beta_out is written once per KV head, by its first row head
+__device__ __forceinline__ bool grp_is_first_head(int g, int G) { return g % G == 0; }
+
 // Generic path for long rows (nb > 1024): keys are recomputed from LDS
 // on every pass instead of being held in registers.
 template <typename KeyFn>
@@ -358,7 +364,9 @@ __device__ uint32_t nth_largest_lds(int nvis, int n, KeyFn key) {
 
 __global__ __launch_bounds__(kThreads) void select_long_kernel(SelectArgs a, int R) {
   extern __shared__ float smem[];
-  const int g = blockIdx.y;
+  const int g = blockIdx.y;        // row head
+  const int gk = g / a.G;          // its KV head
+  const bool beta_writer = grp_is_first_head(g, a.G);
   const int nb = a.nb, D = a.D;
   const int grp = gridDim.x - 1 - blockIdx.x;
   const int i0 = grp * R;
@@ -371,12 +379,12 @@ __global__ __launch_bounds__(kThreads) void select_long_kernel(SelectArgs a, int
   float* qrow = rb + ((nb + 3) & ~3);
   float* red = qrow + R * D;
   float* sc = red + 16;
-  const float* rad = a.rad + (size_t)g * nb;
+  const float* rad = a.rad + (size_t)gk * nb;
   if (a.beta_in) {
-    const float* bi = a.beta_in + (size_t)g * nb;
+    const float* bi = a.beta_in + (size_t)gk * nb;
     for (int j = tid; j < ncols; j += kThreads) rb[j] = rad[j] * bi[j];
-    if (a.beta_out && grp == 0)
-      for (int j = tid; j < nb; j += kThreads) a.beta_out[(size_t)g * nb + j] = bi[j];
+    if (a.beta_out && grp == 0 && beta_writer)
+      for (int j = tid; j < nb; j += kThreads) a.beta_out[(size_t)gk * nb + j] = bi[j];
   } else {
     float sum = 0.f, mx = 0.f;
     for (int j = tid; j < nb; j += kThreads) {
@@ -391,16 +399,17 @@ __global__ __launch_bounds__(kThreads) void select_long_kernel(SelectArgs a, int
     const float top = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
     const float spread = top - mean;
     const bool ok = spread > 1e-6f * top;
-    const int jend = (a.beta_out && grp == 0) ? nb : ncols;
+    const bool write_beta = a.beta_out && grp == 0 && beta_writer;
+    const int jend = write_beta ? nb : ncols;
     for (int j = tid; j < jend; j += kThreads) {
       const float b = ok ? fminf(fmaxf((rad[j] - mean) / spread, 0.f), 1.f) : 0.f;
       if (j < ncols) rb[j] = rad[j] * b;
-      if (a.beta_out && grp == 0) a.beta_out[(size_t)g * nb + j] = b;
+      if (write_beta) a.beta_out[(size_t)gk * nb + j] = b;
     }
   }
   for (int x = tid; x < rows * D; x += kThreads) qrow[x] = a.qrep[((size_t)g * nb + i0) * D + x];
   __syncthreads();
-  const float* cen = a.cen + (size_t)g * nb * D;
+  const float* cen = a.cen + (size_t)gk * nb * D;
   for (int j = tid; j < ncols; j += kThreads) {
     const float4* cj = reinterpret_cast<const float4*>(cen + (size_t)j * D);
     for (int r = 0; r < rows; ++r) {
@@ -541,8 +550,8 @@ int select_rows_per_group(int nb, int D) {
   return 0;
 }
 
-size_t select_score_workspace(int Hkv, int nb) {
-  return nb <= kTriMaxBlocks ? (size_t)Hkv * (tri_off(nb) + nb) * sizeof(float) : 0;
+size_t select_score_workspace(int H, int nb) {
+  return nb <= kTriMaxBlocks ? (size_t)H * (tri_off(nb) + nb) * sizeof(float) : 0;
 }
 
 rbs_status launch_select(const SelectArgs& a, hipStream_t st) {
@@ -552,7 +561,7 @@ rbs_status launch_select(const SelectArgs& a, hipStream_t st) {
   }
   if (a.nb <= kTriMaxBlocks) {
     const int nt = (a.nb + kTile - 1) / kTile;
-    dim3 g1(nt * (nt + 1) / 2 + 1, a.Hkv);
+    dim3 g1(nt * (nt + 1) / 2 + 1, a.H);
     if (a.D == 64)
       hipLaunchKernelGGL(score_tiles_kernel<64>, g1, dim3(kThreads), 0, st, a);
     else
@@ -560,18 +569,18 @@ rbs_status launch_select(const SelectArgs& a, hipStream_t st) {
     rbs_status s = launch_status();
     if (s != RBS_OK) return s;
     const int rows_per_g = (a.nb + 3) / 4;
-    hipLaunchKernelGGL(select_rows_kernel, dim3(rows_per_g * a.Hkv), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(select_rows_kernel, dim3(rows_per_g * a.H), dim3(kThreads), 0, st, a);
   } else {
     const int R = select_rows_per_group(a.nb, a.D);
     if (R <= 0) return RBS_E_UNSUPPORTED;
     const size_t shmem =
         ((size_t)((a.nb + 3) & ~3) + (size_t)R * a.D + 16 + (size_t)R * ((a.nb + 3) & ~3)) * 4;
-    dim3 grid((a.nb + R - 1) / R, a.Hkv);
+    dim3 grid((a.nb + R - 1) / R, a.H);
     hipLaunchKernelGGL(select_long_kernel, grid, dim3(kThreads), shmem, st, a, R);
   }
   rbs_status s = launch_status();
   if (s != RBS_OK) return s;
-  const int nrows = a.Hkv * a.nb;
+  const int nrows = a.H * a.nb;
   hipLaunchKernelGGL(compact_kernel, dim3((nrows + kCompactRows - 1) / kCompactRows),
                      dim3(kThreads), 0, st, a.counts, a.lists, a.stride, nrows, a.row_ptr,
                      a.col_idx);

@@ -5,7 +5,8 @@
 // (largest key-to-centroid distance); "The Fix" scores blocks with a query q
 // and ||q||_2. One workgroup handles one (KV head g, block b) and makes a
 // single pass over HBM: the group's query rows of block b are summed into the
-// representative query, and the key tile stays in registers between the mean
+// representative query (one per group, and optionally one per query head for
+// per-head selection), and the key tile stays in registers between the mean
 // and the distance pass.
 //
 // Bound: HBM. Algorithmic bytes per (g, b): B*(G+1)*D*sizeof(T) read,
@@ -44,7 +45,7 @@ template <typename T, int D, int MAXV>
 __global__ __launch_bounds__(kThreads) void block_stats_kernel(
     const T* __restrict__ q, const T* __restrict__ k, int S, int Hq, int Hkv, int B,
     float* __restrict__ cen, float* __restrict__ rad, float* __restrict__ qrep,
-    float* __restrict__ qnorm) {
+    float* __restrict__ qnorm, float* __restrict__ qrep_h, float* __restrict__ qnorm_h) {
   constexpr int EPV = Vec16<T>::N;        // elements per 16-byte vector
   constexpr int KVEC = D / EPV;           // vectors per key row (divides 256)
   extern __shared__ float smem[];
@@ -59,12 +60,13 @@ __global__ __launch_bounds__(kThreads) void block_stats_kernel(
 
   // ---------------- representative query: mean over L tokens x G heads ----
   const int VR = G * KVEC;                            // vectors per token row of the group
-  // LDS: qred [qslots][EPV] | red [16] | kred [256][EPV] | cvec [D]
+  // LDS: qred [qslots][EPV] | red [16] | kred [256][EPV] | cvec [D] | hsq [G D / 64]
   const int qslots = VR <= kThreads ? (kThreads / VR) * VR : VR;
   float* qred = smem;
   float* red = qred + qslots * EPV;
   float* kred = red + 16;
   float* cvec = kred + kThreads * EPV;
+  float* hsq = cvec + D;  // per 64-element chunk of the per-head means: sum of squares
   {
     const int TP = VR <= kThreads ? kThreads / VR : 1;   // tokens per pass
     const int NV = VR <= kThreads ? 1 : (VR + kThreads - 1) / kThreads;
@@ -110,17 +112,36 @@ __global__ __launch_bounds__(kThreads) void block_stats_kernel(
           s += qred[slot * EPV + (tid % EPV)];
         }
       qd = s / (float)(G * L);
-      qrep[((size_t)g * nb + b) * D + tid] = qd;
+      if (qrep) qrep[((size_t)g * nb + b) * D + tid] = qd;
     }
     float sq = wave_sum(qd * qd);
     if ((tid & 63) == 0) red[tid >> 6] = sq;
+    if (qrep_h) {
+      // per query head hl of the group: the mean over the block's tokens; a
+      // wave's 64 elements belong to one head (64 divides D)
+      for (int x = tid; x < G * D; x += kThreads) {
+        const int hl = x / D, d = x % D;
+        float sh = 0.f;
+        for (int to = 0; to < TP; ++to) sh += qred[(to * VR + hl * KVEC + d / EPV) * EPV + d % EPV];
+        const float m = sh / (float)L;
+        qrep_h[((size_t)(g * G + hl) * nb + b) * D + d] = m;
+        const float w2 = wave_sum(m * m);
+        if ((tid & 63) == 0) hsq[x >> 6] = w2;
+      }
+    }
   }
   __syncthreads();
-  if (tid == 0) {
+  if (tid == 0 && qnorm) {
     float s = 0.f;
     for (int w = 0; w < kThreads / 64; ++w) s += red[w];
     qnorm[(size_t)g * nb + b] = sqrtf(s);
   }
+  if (qrep_h)
+    for (int x = tid; x < G; x += kThreads) {
+      float s2 = 0.f;
+      for (int c = 0; c < D / 64; ++c) s2 += hsq[x * (D / 64) + c];
+      qnorm_h[(size_t)(g * G + x) * nb + b] = sqrtf(s2);
+    }
 
   // ---------------- key centroid and radius --------------------------------
   const int dv = tid % KVEC;                 // this thread's vector column
@@ -188,7 +209,8 @@ __global__ __launch_bounds__(kThreads) void block_stats_kernel(
 
 template <typename T, int D>
 rbs_status launch_typed(const void* q, const void* k, int S, int Hq, int Hkv, int B, float* cen,
-                        float* rad, float* qrep, float* qnorm, hipStream_t st) {
+                        float* rad, float* qrep, float* qnorm, float* qrep_h, float* qnorm_h,
+                        hipStream_t st) {
   constexpr int EPV = 16 / sizeof(T);
   constexpr int KVEC = D / EPV;
   const int nb = (S + B - 1) / B;
@@ -196,10 +218,11 @@ rbs_status launch_typed(const void* q, const void* k, int S, int Hq, int Hkv, in
   dim3 grid(nb, Hkv);
   const int VR = (Hq / Hkv) * KVEC;
   const int qslots = VR <= kThreads ? (kThreads / VR) * VR : VR;
-  const size_t shmem = ((size_t)qslots * EPV + 16 + kThreads * EPV + D) * sizeof(float);
+  const size_t shmem =
+      ((size_t)qslots * EPV + 16 + kThreads * EPV + D + (Hq / Hkv) * (D / 64)) * sizeof(float);
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(kThreads), shmem, st, (const T*)q, (const T*)k, S, Hq,
-                       Hkv, B, cen, rad, qrep, qnorm);
+                       Hkv, B, cen, rad, qrep, qnorm, qrep_h, qnorm_h);
     return launch_status();
   };
   if (need <= 2) return go(block_stats_kernel<T, D, 2>);
@@ -213,13 +236,15 @@ rbs_status launch_typed(const void* q, const void* k, int S, int Hq, int Hkv, in
 
 rbs_status launch_block_stats(rbs_dtype dt, const void* q, const void* k, int S, int Hq, int Hkv,
                               int D, int B, float* cen, float* rad, float* qrep, float* qnorm,
-                              hipStream_t st) {
+                              float* qrep_h, float* qnorm_h, hipStream_t st) {
   if (dt == RBS_DT_BF16) {
-    if (D == 64) return launch_typed<uint16_t, 64>(q, k, S, Hq, Hkv, B, cen, rad, qrep, qnorm, st);
-    return launch_typed<uint16_t, 128>(q, k, S, Hq, Hkv, B, cen, rad, qrep, qnorm, st);
+    if (D == 64)
+      return launch_typed<uint16_t, 64>(q, k, S, Hq, Hkv, B, cen, rad, qrep, qnorm, qrep_h, qnorm_h, st);
+    return launch_typed<uint16_t, 128>(q, k, S, Hq, Hkv, B, cen, rad, qrep, qnorm, qrep_h, qnorm_h, st);
   }
-  if (D == 64) return launch_typed<float, 64>(q, k, S, Hq, Hkv, B, cen, rad, qrep, qnorm, st);
-  return launch_typed<float, 128>(q, k, S, Hq, Hkv, B, cen, rad, qrep, qnorm, st);
+  if (D == 64)
+    return launch_typed<float, 64>(q, k, S, Hq, Hkv, B, cen, rad, qrep, qnorm, qrep_h, qnorm_h, st);
+  return launch_typed<float, 128>(q, k, S, Hq, Hkv, B, cen, rad, qrep, qnorm, qrep_h, qnorm_h, st);
 }
 
 }  // namespace rbs

@@ -124,9 +124,45 @@ rbs_status rbs_select(const float* k_centroid, const float* k_radius, const floa
 
 /* Number of col_idx entries rbs_select may write for these arguments (host
  * only, no device work): Hkv * sum_i min(i+1, n_c(i) + n_r(i) + 1 + sink).
- * Returns -1 on invalid arguments. */
+ * For rbs_select_per_head pass n_q_heads as the first argument (one list per
+ * query head). Returns -1 on invalid arguments. */
 int64_t rbs_select_capacity(int32_t n_kv_heads, int32_t n_blocks, double keep_ratio_centroid,
                             double keep_ratio_rescue, uint32_t flags);
+
+/*
+ * Per-query-head selection (the other reading of the representative query):
+ * one representative per (query head, query block) instead of one per (GQA
+ * group, query block), and one block list per query head. The rescue and
+ * centroid scores of row (h, i) use q_rep_head[h][i] with the centroids,
+ * radii and beta of KV head g = h / (Hq / Hkv); budgets, forced blocks, ties
+ * and beta are as in rbs_select. A group's heads no longer share one list, so
+ * fewer K/V tiles are shared between them in attention.
+ *
+ * rbs_block_stats_per_head: as rbs_block_stats, but instead of the group
+ *   representative it writes, for query head h and block b,
+ *     q_rep_head[h][b][:]    = mean over the block's tokens of Q[t][h][:]
+ *     q_rep_head_norm[h][b]  = ||q_rep_head[h][b][:]||_2
+ *   (fp32 [Hq][nb][D] and [Hq][nb]); k_centroid and k_radius as there. Q and K
+ *   are read once. Same arguments, support and errors.
+ * rbs_select_per_head: as rbs_select with rows r = h * nb + i for h < n_q_heads
+ *   (row_ptr [Hq*nb + 1]); q_rep_head [Hq][nb][D], q_rep_head_norm [Hq][nb];
+ *   k_centroid, k_radius, beta_in and beta_out stay per KV head. Errors as
+ *   rbs_select, plus RBS_E_ARG when n_q_heads % n_kv_heads != 0.
+ * blocksparse_attn_fwd_per_head: as blocksparse_attn_fwd, but query head h of
+ *   block i attends to the blocks of CSR row h * nb + i.
+ */
+rbs_status rbs_block_stats_per_head(rbs_dtype dt, const void* q, const void* k, int32_t seqlen,
+                                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                    int32_t block, float* k_centroid, float* k_radius,
+                                    float* q_rep_head, float* q_rep_head_norm, void* stream);
+
+rbs_status rbs_select_per_head(const float* k_centroid, const float* k_radius,
+                               const float* q_rep_head, const float* q_rep_head_norm,
+                               const float* beta_in, int32_t n_q_heads, int32_t n_kv_heads,
+                               int32_t n_blocks, int32_t head_dim, double keep_ratio_centroid,
+                               double keep_ratio_rescue, uint32_t flags, float* beta_out,
+                               int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                               void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
  * blocksparse_attn_fwd - causal GQA attention over the selected key blocks.
@@ -155,6 +191,14 @@ rbs_status blocksparse_attn_fwd(rbs_dtype dt, const void* q, const void* k, cons
                                 int32_t head_dim, int32_t block, const int32_t* row_ptr,
                                 const int32_t* col_idx, float softmax_scale, void* out,
                                 float* lse, void* stream);
+
+/* Per-query-head block lists (see rbs_select_per_head): row h * nb + i. */
+rbs_status blocksparse_attn_fwd_per_head(rbs_dtype dt, const void* q, const void* k,
+                                         const void* v, int32_t seqlen, int32_t n_q_heads,
+                                         int32_t n_kv_heads, int32_t head_dim, int32_t block,
+                                         const int32_t* row_ptr, const int32_t* col_idx,
+                                         float softmax_scale, void* out, float* lse,
+                                         void* stream);
 
 /*
  * block_mask_attn_fwd - Block-attention prefill with position re-encoding.

@@ -166,3 +166,29 @@ def test_block_mask_workspace_query(L):
     assert query(qrb=31232 - 100, **kw) == keys + 1 * 32 * 4 * 128 * 132 * 4
     # a misaligned workspace is refused
     assert bmask(L, ws=P + 16, wsz=need, **kw) == E.RBS_E_ARG
+
+
+def test_per_head_entry_points_validate_before_launch(L):
+    sz = ctypes.c_size_t(0)
+    # size query: one list per query head (8 heads x 300 rows' worth of workspace)
+    r = L.rbs_select_per_head(None, None, None, None, None, 8, 2, 300, 128, 0.1, 0.1, 0, None,
+                              None, None, 0, None, ctypes.byref(sz), None)
+    assert r == E.RBS_OK and sz.value > 0
+    sz2 = ctypes.c_size_t(0)
+    r = L.rbs_select(None, None, None, None, None, 8, 300, 128, 0.1, 0.1, 0, None, None, None, 0,
+                     None, ctypes.byref(sz2), None)
+    assert r == E.RBS_OK and sz2.value == sz.value    # same rows, same workspace
+    # query heads not a multiple of KV heads
+    r = L.rbs_select_per_head(None, None, None, None, None, 7, 2, 300, 128, 0.1, 0.1, 0, None,
+                              None, None, 0, None, ctypes.byref(sz), None)
+    assert r == E.RBS_E_ARG
+    # stats: missing per-head outputs, bad head dim
+    r = L.rbs_block_stats_per_head(0, P, P, 300, 8, 2, 128, 128, P, P, None, None, None)
+    assert r == E.RBS_E_ARG
+    r = L.rbs_block_stats_per_head(0, P, P, 300, 8, 2, 96, 128, P, P, P, P, None)
+    assert r == E.RBS_E_UNSUPPORTED
+    # attention: the same shape checks as the group call
+    r = L.blocksparse_attn_fwd_per_head(0, P, P, P, 300, 8, 2, 96, 128, P, P, 0.0, P, None, None)
+    assert r == E.RBS_E_UNSUPPORTED
+    r = L.blocksparse_attn_fwd_per_head(0, P, P, P, 0, 8, 2, 128, 128, P, P, 0.0, P, None, None)
+    assert r == E.RBS_OK
