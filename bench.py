@@ -218,6 +218,47 @@ def main():
         }
         log(f"dense causal attention {t_dense:.2f} ms -> speedup {t_dense / t_attn:.2f}x")
         del rpd_t, cid_t
+        # per-query-head selection (the other reading of the representative
+        # query): one block list per query head, same keep ratios
+        wsh = torch.empty(96 << 20, dtype=torch.uint8, device="cuda")
+        outh = torch.empty_like(t["q"])
+
+        def step_per_head():
+            st_h = rbs.rbs_block_stats_per_head(t["q"], t["k"], B)
+            rp_, ci_, _ = rbs.rbs_select_per_head(*st_h, w.keep_ratio_centroid,
+                                                  w.keep_ratio_rescue, sink=w.sink, workspace=wsh)
+            rbs.blocksparse_attn_fwd_per_head(t["q"], t["k"], t["v"], B, rp_, ci_, out=outh)
+            return rp_, ci_
+
+        for _ in range(2):
+            step_per_head()
+        torch.cuda.synchronize()
+        evh = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(5)]
+        for s_ in range(5):
+            evh[s_][0].record(stream)
+            st_h = rbs.rbs_block_stats_per_head(t["q"], t["k"], B)
+            evh[s_][1].record(stream)
+            rp_h2, ci_h2, _ = rbs.rbs_select_per_head(*st_h, w.keep_ratio_centroid,
+                                                      w.keep_ratio_rescue, sink=w.sink,
+                                                      workspace=wsh)
+            evh[s_][2].record(stream)
+            rbs.blocksparse_attn_fwd_per_head(t["q"], t["k"], t["v"], B, rp_h2, ci_h2, out=outh)
+            evh[s_][3].record(stream)
+        torch.cuda.synchronize()
+        ph = [float(np.mean([evh[s_][a].elapsed_time(evh[s_][a + 1]) for s_ in range(5)]))
+              for a in range(3)]
+        rph = rp_h2.cpu().numpy().astype(np.int64)
+        cih = ci_h2[:int(rph[-1])].cpu().numpy()
+        flops_h = 4.0 * D * selected_pairs(rph, cih, S, B, Hq)
+        result["per_query_head_selection"] = {
+            "stats_ms": round(ph[0], 4), "select_ms": round(ph[1], 4), "attn_ms": round(ph[2], 4),
+            "attn_flops": flops_h, "attn_tflops": round(flops_h / (ph[2] * 1e-3) / 1e12, 1),
+            "csr_nnz": int(rph[-1]),
+            "attn_ms_over_group_reading": round(ph[2] / t_attn, 3),
+        }
+        log(f"per-query-head selection: stats {ph[0]:.3f} select {ph[1]:.3f} attn {ph[2]:.3f} ms "
+            f"({flops_h / (ph[2] * 1e-3) / 1e12:.1f} TFLOP/s, {int(rph[-1])} CSR entries)")
+        del wsh, outh
         # Block-attention RAG workload
         wr = inputs.rag_bf16_31k()
         tr = device.upload(wr)
