@@ -55,7 +55,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the dense ratio and the Block-attention workload")
-    ap.add_argument("--cpu-rows", type=int, default=256,
+    ap.add_argument("--cpu-rows", type=int, default=448,
                     help="(KV head, query block) rows of the oracle's attention to time")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (counter calibration)")
