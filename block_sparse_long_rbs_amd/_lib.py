@@ -45,6 +45,9 @@ _SIGS = {
                                                      _vp, _vp, _vp]),
     "blocksparse_attn_fwd": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
                                             _c_i32, _c_i32, _vp, _vp, _c_f32, _vp, _vp, _vp]),
+    "blocksparse_attn_fwd_fp8": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                _c_i32, _vp, _vp, _c_f32, _c_f32, _c_f32, _c_f32,
+                                                _vp, _vp, _vp]),
     "block_mask_attn_fwd": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
                                            _c_i32, _c_i32, ctypes.POINTER(_c_i32),
                                            ctypes.POINTER(_c_i32), _c_f32, _c_i32, _c_f32, _vp,
@@ -244,6 +247,28 @@ def blocksparse_attn_fwd(q, k, v, block: int, row_ptr, col_idx, softmax_scale: f
         _dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), S, Hq, Hkv, D, block,
         row_ptr.data_ptr(), col_idx.data_ptr(), softmax_scale, out.data_ptr(), _ptr(lse),
         _stream(q)))
+    return out, lse
+
+
+def blocksparse_attn_fwd_fp8(q, k, v, block: int, row_ptr, col_idx, q_descale: float = 1.0,
+                             k_descale: float = 1.0, v_descale: float = 1.0,
+                             softmax_scale: float = 0.0, want_lse: bool = False,
+                             out: Optional[torch.Tensor] = None):
+    """blocksparse_attn_fwd on fp8 (torch.float8_e4m3fn) Q, K, V with per-tensor
+    dequantisation factors -> (bf16 out, lse or None)."""
+    _need_cuda(q, k, v, row_ptr, col_idx)
+    for t in (q, k, v):
+        if t.dtype != torch.float8_e4m3fn:
+            raise TypeError(f"blocksparse_attn_fwd_fp8 takes float8_e4m3fn tensors, got {t.dtype}")
+    S, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((Hq, S), dtype=torch.float32, device=q.device) if want_lse else None
+    _check("blocksparse_attn_fwd_fp8", lib().blocksparse_attn_fwd_fp8(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), S, Hq, Hkv, D, block, row_ptr.data_ptr(),
+        col_idx.data_ptr(), softmax_scale, q_descale, k_descale, v_descale, out.data_ptr(),
+        _ptr(lse), _stream(q)))
     return out, lse
 
 

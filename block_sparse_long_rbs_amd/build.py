@@ -21,7 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librbs.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "stats.hip", "select.hip", "attn_bf16.hip", "attn_f32.hip", "rope.hip"]
+SOURCES = ["api.cpp", "stats.hip", "select.hip", "attn_bf16.hip", "attn_fp8.hip", "attn_f32.hip",
+           "rope.hip"]
 
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

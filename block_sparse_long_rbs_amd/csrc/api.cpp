@@ -152,11 +152,11 @@ rbs_status select_common(const float* k_centroid, const float* k_radius, const f
 }  // namespace
 
 namespace {
-rbs_status attn_common(rbs_dtype dt, const void* q, const void* k, const void* v, int32_t seqlen,
-                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block,
-                       const int32_t* row_ptr, const int32_t* col_idx, float softmax_scale,
-                       void* out, float* lse, bool per_head, void* stream) {
-  if (dt != RBS_DT_BF16 && dt != RBS_DT_F32) return RBS_E_ARG;
+// Checks shared by the CSR attention entries (every dtype); fills a.
+rbs_status attn_args(const void* q, const void* k, const void* v, int32_t seqlen,
+                     int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block,
+                     const int32_t* row_ptr, const int32_t* col_idx, float softmax_scale,
+                     void* out, float* lse, bool per_head, AttnArgs& a) {
   if (seqlen < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || block <= 0)
     return RBS_E_ARG;
   if (n_q_heads % n_kv_heads != 0) return RBS_E_ARG;
@@ -164,12 +164,9 @@ rbs_status attn_common(rbs_dtype dt, const void* q, const void* k, const void* v
                      !aligned(row_ptr, 4) || !aligned(col_idx, 4) || (lse && !aligned(lse, 4))))
     return RBS_E_ARG;
   if (isnan(softmax_scale) || isinf(softmax_scale)) return RBS_E_ARG;
-  const bool bf = dt == RBS_DT_BF16;
   if (!((head_dim == 64 || head_dim == 128) && (block == 64 || block == 128)))
     return RBS_E_UNSUPPORTED;
   if ((int64_t)seqlen * n_q_heads * head_dim > ((int64_t)1 << 40)) return RBS_E_UNSUPPORTED;
-  if (seqlen == 0) return RBS_OK;
-  AttnArgs a;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -184,6 +181,19 @@ rbs_status attn_common(rbs_dtype dt, const void* q, const void* k, const void* v
   a.B = block;
   a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
   a.per_head = per_head ? 1 : 0;
+  return RBS_OK;
+}
+
+rbs_status attn_common(rbs_dtype dt, const void* q, const void* k, const void* v, int32_t seqlen,
+                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block,
+                       const int32_t* row_ptr, const int32_t* col_idx, float softmax_scale,
+                       void* out, float* lse, bool per_head, void* stream) {
+  if (dt != RBS_DT_BF16 && dt != RBS_DT_F32) return RBS_E_ARG;
+  AttnArgs a;
+  const rbs_status st = attn_args(q, k, v, seqlen, n_q_heads, n_kv_heads, head_dim, block, row_ptr,
+                                  col_idx, softmax_scale, out, lse, per_head, a);
+  if (st != RBS_OK || seqlen == 0) return st;
+  const bool bf = dt == RBS_DT_BF16;
   // bf16 at head dim 128 and block 128 runs on the matrix cores; every other
   // supported shape on the vector-ALU kernel
   if (bf && head_dim == 128 && block == 128) return launch_attn_bf16_csr(a, as_stream(stream));
@@ -266,6 +276,22 @@ rbs_status blocksparse_attn_fwd(rbs_dtype dt, const void* q, const void* k, cons
                                 float* lse, void* stream) {
   return attn_common(dt, q, k, v, seqlen, n_q_heads, n_kv_heads, head_dim, block, row_ptr,
                      col_idx, softmax_scale, out, lse, false, stream);
+}
+
+rbs_status blocksparse_attn_fwd_fp8(const void* q, const void* k, const void* v, int32_t seqlen,
+                                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                    int32_t block, const int32_t* row_ptr, const int32_t* col_idx,
+                                    float softmax_scale, float q_descale, float k_descale,
+                                    float v_descale, void* out, float* lse, void* stream) {
+  AttnArgs a;
+  const rbs_status st = attn_args(q, k, v, seqlen, n_q_heads, n_kv_heads, head_dim, block, row_ptr,
+                                  col_idx, softmax_scale, out, lse, false, a);
+  if (st != RBS_OK) return st;
+  for (const float d : {q_descale, k_descale, v_descale})
+    if (!(d > 0.f) || isinf(d)) return RBS_E_ARG;
+  if (head_dim != 128 || block != 128) return RBS_E_UNSUPPORTED;
+  if (seqlen == 0) return RBS_OK;
+  return launch_attn_fp8_csr(a, q_descale, k_descale, v_descale, as_stream(stream));
 }
 
 rbs_status blocksparse_attn_fwd_per_head(rbs_dtype dt, const void* q, const void* k,

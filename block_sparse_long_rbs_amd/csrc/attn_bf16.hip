@@ -36,62 +36,16 @@
 //
 // Bound: matrix cores. Algorithmic flops per (query row, key) pair: 4*D.
 
-#include <math.h>
-
-#include "rbs_common.h"
+#include "attn_tiles.h"
 
 namespace rbs {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+using namespace tiles;
 
-constexpr int D = 128;
-constexpr int TILE = 128;            // keys per tile and query rows per workgroup
-constexpr int kThreads = 256;
 constexpr int ROWB = D * 2;          // bytes per K or V row in LDS
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
-
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
-  const bf16x2_t v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
-}
-
-// Workgroup barrier for LDS hand-offs: this wave's LDS reads/writes are
-// complete, then s_barrier. No memory fence, so tile DMAs (vector-memory
-// writes into LDS) stay in flight across it; their completion is awaited
-// explicitly with wait_vmcnt before the barrier that publishes them.
-__device__ __forceinline__ void lds_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// One 16-byte-per-lane DMA from global memory (uniform base + per-lane 32-bit
-// byte offset) into LDS at lds_addr + 16*lane (the LDS address goes in M0,
-// which the compiler loads for the statement). Issued as inline asm so that
-// the compiler does not treat it as a pending LDS write (it would otherwise
-// wait for every in-flight tile before each LDS read); completion is awaited
-// explicitly with wait_vmcnt.
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(lds_addr)
-               : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
 
 // 16-byte chunk swizzles in LDS: chunk c of K row r sits at slot c ^ (r & 15)
 // (fragments read 16 rows x one chunk), chunk c of V row r at c ^ ((r & 3) << 2)
@@ -131,40 +85,6 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, size_
   }
 }
 
-// Lanes l and l^32 hold the same query row: combine their values.
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Work unit decode: XCD-aware, heaviest (highest) query tiles first. The G
-// heads (times the key-range chunks, if any) of one (KV head, query tile)
-// unit get neighbouring slots on one XCD.
-struct Unit {
-  int g, h, qt, c;
-};
-__device__ __forceinline__ bool decode_unit(int x, int G, int Hkv, int qt_lo, int qt_hi, int C,
-                                            Unit& u) {
-  const int per = G * C;
-  const int xcd = x & 7;
-  const int slot = x >> 3;
-  const int hg = slot % per;
-  const int uo = (slot / per) * 8 + xcd;
-  const int n_units = Hkv * (qt_hi - qt_lo);
-  if (uo >= n_units) return false;
-  u.qt = qt_hi - 1 - uo / Hkv;
-  u.g = uo % Hkv;
-  u.h = u.g * G + hg % G;
-  u.c = hg / G;
-  return true;
-}
-
 __device__ __forceinline__ void load_q(const uint16_t* __restrict__ Q, int S, int Hq, int h,
                                        int qt, bf16x8_t* qf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -176,29 +96,6 @@ __device__ __forceinline__ void load_q(const uint16_t* __restrict__ Q, int S, in
     if (t < S) u = *reinterpret_cast<const uint4*>(Q + ((size_t)t * Hq + h) * D + 16 * c + 8 * hh);
     qf[c] = as_bf16x8(u);
   }
-}
-
-__device__ __forceinline__ void store_out(uint16_t* __restrict__ O, float* __restrict__ lse, int S,
-                                          int Hq, int h, int qt, int row_begin, const f32x16_t* o,
-                                          float m_run, float l_run) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int m32 = lane & 31, hh = lane >> 5;
-  const int t = qt * TILE + wave * 32 + m32;
-  const float l = pair_sum(l_run);
-  if (t >= S || t < row_begin) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  uint16_t* orow = O + ((size_t)t * Hq + h) * D;
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int d = db * 32 + 8 * rg + 4 * hh;
-      const uint2 v = make_uint2(cvt_pk_bf16(o[db][4 * rg] * inv, o[db][4 * rg + 1] * inv),
-                                 cvt_pk_bf16(o[db][4 * rg + 2] * inv, o[db][4 * rg + 3] * inv));
-      *reinterpret_cast<uint2*>(orow + d) = v;
-    }
-  if (lse && hh == 0)
-    lse[(size_t)h * S + t] = l > 0.f ? (m_run + __log2f(l)) * 0.69314718055994530942f : -INFINITY;
 }
 
 // Unnormalised partial result of one key-range chunk: for each of the tile's
@@ -274,28 +171,6 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a, SegA
     a.lse[(size_t)h * a.S + t] =
         L > 0.f ? (M + __log2f(L)) * 0.69314718055994530942f : -INFINITY;
 }
-
-// Key tiles of one unit in CSR mode: the row's block list, staged in LDS 256
-// entries at a time (a vector load inside the tile loop would make every wait
-// drain the in-flight tile DMAs); entries outside 0..qt are skipped.
-struct CsrTiles {
-  const int32_t* col_idx;
-  int e, e1, cb, qt;
-  int* lst;
-  __device__ int next(int e_from) {
-    for (e = e_from; e < e1; ++e) {
-      if (e - cb >= kThreads) {  // refill: every wave reaches this point together
-        lds_barrier();
-        cb = e;
-        lst[threadIdx.x] = (cb + (int)threadIdx.x < e1) ? col_idx[cb + threadIdx.x] : -1;
-        lds_barrier();
-      }
-      const int j = lst[e - cb];
-      if (j >= 0 && j <= qt) return j;
-    }
-    return -1;
-  }
-};
 
 // Key tiles of one unit in segment mode: jlo..jhi.
 struct SegTiles {
@@ -508,13 +383,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
                o, m_run, l_run);
   else
     store_out(static_cast<uint16_t*>(a.out), a.lse, a.S, a.Hq, u.h, u.qt,
-              SEG ? seg.q_row_begin : 0, o, m_run, l_run);
-}
-
-inline int attn_grid(int Hq, int Hkv, int n_qt, int chunks) {
-  const int G = Hq / Hkv;
-  const int units = Hkv * (n_qt > 0 ? n_qt : 0);
-  return ((units + 7) / 8) * 8 * G * chunks;
+              SEG ? seg.q_row_begin : 0, o, m_run, l_run, 1.0f);
 }
 
 }  // namespace

@@ -1,0 +1,303 @@
+// Block-sparse causal GQA attention with fp8 inputs: Q, K and V in the OCP
+// e4m3 format, each with one dequantisation factor, and a bf16 output; head
+// dim 128, key tile = block = 128 tokens, on gfx950 matrix cores
+// (v_mfma_f32_32x32x64_f8f6f4: fp8 x fp8 products of depth 64, fp32 sums).
+// RBS-Attention explainer, "The Fix": the selection's CSR block lists drive a
+// standard block-sparse attention; this is that attention for fp8 caches.
+//
+// Work decomposition, CSR iteration, online softmax and XCD-aware grid are
+// those of the bf16 kernel (attn_bf16.hip). Per key tile:
+//   S^T = K Q^T: per 32-key block, two products of depth 64. A lane holds 32
+//     consecutive head-dim bytes of its key row (two 16-byte LDS reads) and
+//     of its query row (registers). The MFMA pairs A and B bytes by the same
+//     (lane half, byte) position, so one common byte order serves both.
+//   P = 2^(s - m) rounded to e4m3 (nearest even) straight from the score
+//     registers. e4m3 tops out at 448 and has no infinity (larger values
+//     become NaN), so the running max is raised as soon as a lane's share of
+//     a tile's row sum exceeds 2^8: every P stays <= 256.
+//   O^T += V^T P^T: per 32-wide slice of the head dim and 64-key chunk, one
+//     product. The V^T operand comes from 8-bit transposing LDS reads
+//     (ds_read_b64_tr_b8), ordered so that byte j of a lane pairs with the
+//     key that byte j of the P operand holds.
+// Scores are scaled by softmax_scale * q_descale * k_descale, the output by
+// v_descale. K and V tiles are 16 KB each (128 bytes per key row), moved HBM
+// -> LDS by global_load_lds_dwordx4 with explicit vector-memory counts as in
+// the bf16 kernel (4 loads per wave per tile instead of 8).
+//
+// Bound: matrix cores. Algorithmic flops per (query row, key) pair: 4*D.
+
+#include "attn_tiles.h"
+
+namespace rbs {
+namespace {
+
+using namespace tiles;
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
+
+constexpr int ROW8 = D;  // bytes per K or V row in LDS
+
+// 32x32 block += A (32 x 64, e4m3) * B (64 x 32, e4m3). Zero scale operands
+// select the plain (unscaled) instruction.
+__device__ __forceinline__ f32x16_t mfma_fp8(const v8i_t& a, const v8i_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// 16-byte chunk swizzles in LDS (8 chunks per 128-byte row): chunk c of K row
+// r sits at slot c ^ ((r >> 1) & 7) (fragment reads take 32 rows x one chunk),
+// chunk c of V row r at c ^ (((r >> 1) & 3) << 1) (transposing reads take 16
+// rows x two neighbouring chunks). Either way each read spreads evenly over
+// the LDS banks.
+__device__ __forceinline__ int k_swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int v_swz(int r) { return ((r >> 1) & 3) << 1; }
+
+// DMA one 128 x 128 e4m3 tile (tokens key0.., one KV head; src points at that
+// head's token 0) into LDS. Each of the 4 waves issues 4 loads of 1 KB (8
+// rows); lane l of a load lands at slot l & 7 of row l >> 3, so it fetches
+// the logical chunk that the swizzle puts there. Rows past the sequence end
+// repeat the last row (finite values; their scores are masked).
+template <bool IS_V>
+__device__ __forceinline__ void dma_tile8(const uint8_t* __restrict__ src, size_t rs, int S,
+                                          int key0, char* lds) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r8 = lane >> 3, pc = lane & 7;
+  const uint32_t dst = lds_u32(lds) + wave * 4 * 1024;
+  const int row0 = key0 + wave * 32;
+  const uint32_t rsb = (uint32_t)rs;  // bytes per token row
+  if (row0 + 32 <= S) {
+    const uint8_t* base = src + (size_t)row0 * rs;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int r = wave * 32 + it * 8 + r8;  // row within the tile
+      const int lc = pc ^ (IS_V ? v_swz(r) : k_swz(r));
+      dma16(base + (size_t)(it * 8) * rs, r8 * rsb + lc * 16, dst + it * 1024);
+    }
+  } else {
+    // ragged end: rows are clamped to S - 1, offsets taken from min(row0, S - 1)
+    const int r0 = min(row0, S - 1);
+    const uint8_t* cbase = src + (size_t)r0 * rs;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int r = wave * 32 + it * 8 + r8;
+      const int lc = pc ^ (IS_V ? v_swz(r) : k_swz(r));
+      const int tok = min(row0 + it * 8 + r8, S - 1);
+      dma16(cbase, (uint32_t)(tok - r0) * rsb + lc * 16, dst + it * 1024);
+    }
+  }
+}
+
+// Q fragments of one query tile: for depth chunk kc (head dims 64 kc ..
+// 64 kc + 63), lane l holds bytes 64 kc + 32 (l >> 5) .. + 31 of its query
+// row. Rows past the end are zero.
+__device__ __forceinline__ void load_q8(const uint8_t* __restrict__ Q, int S, int Hq, int h, int qt,
+                                        v8i_t* qf) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = qt * TILE + wave * 32 + (lane & 31);
+  const int hh = lane >> 5;
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+    uint4 u0 = make_uint4(0, 0, 0, 0), u1 = make_uint4(0, 0, 0, 0);
+    if (t < S) {
+      const uint8_t* p = Q + ((size_t)t * Hq + h) * D + 64 * kc + 32 * hh;
+      u0 = *reinterpret_cast<const uint4*>(p);
+      u1 = *reinterpret_cast<const uint4*>(p + 16);
+    }
+    qf[kc] = (v8i_t){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
+                     (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void attn_fp8_kernel(AttnArgs a,
+                                                               const int32_t* __restrict__ row_ptr,
+                                                               const int32_t* __restrict__ col_idx,
+                                                               float scale_log2, float out_scale) {
+  __shared__ __attribute__((aligned(1024))) char Ks[TILE * ROW8];
+  __shared__ __attribute__((aligned(1024))) char Vs[TILE * ROW8];
+  __shared__ int lst[kThreads];
+  const int G = a.Hq / a.Hkv;
+  const int nq = (a.S + TILE - 1) / TILE;
+  Unit u;
+  if (!decode_unit(blockIdx.x, G, a.Hkv, 0, nq, 1, u)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m32 = lane & 31, hh = lane >> 5;
+  const size_t rs = (size_t)a.Hkv * D;
+  const uint8_t* Kg = static_cast<const uint8_t*>(a.k) + (size_t)u.g * D;
+  const uint8_t* Vg = static_cast<const uint8_t*>(a.v) + (size_t)u.g * D;
+
+  CsrTiles csr{col_idx, 0, 0, 0, u.qt, lst};
+  {
+    const int row = (a.per_head ? u.h : u.g) * nq + u.qt;
+    csr.e = row_ptr[row];
+    csr.e1 = row_ptr[row + 1];
+    csr.cb = csr.e;
+    lst[threadIdx.x] = (csr.e + (int)threadIdx.x < csr.e1) ? col_idx[csr.e + threadIdx.x] : -1;
+    lds_barrier();
+  }
+
+  v8i_t qf[2];
+  load_q8(static_cast<const uint8_t*>(a.q), a.S, a.Hq, u.h, u.qt, qf);
+  f32x16_t o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = (f32x16_t){};
+  float m_run = 0.f, l_run = 0.f;
+  bool first = true;
+
+  // per-lane LDS offsets. K fragment of key block kb, depth chunk kc: row
+  // kb * 32 + m32, logical chunks 4 kc + 2 hh and 4 kc + 2 hh + 1.
+  const int kswz = k_swz(m32);  // rows kb * 32 + m32 share bits 1..3 with m32
+  // V^T fragment, read q of 4 for depth slice db and key chunk kc: this lane
+  // supplies row 64 kc + 16 q + vrow (q's two bits put 32 (q >> 1) + 16 (q & 1)
+  // = 16 q) and byte 32 db + 16 (g & 1) + 8 (s & 1) of it, with g = lane / 16,
+  // s = lane % 16 (a transposing read hands lane i of a 16-lane group byte
+  // i & 7 of the 8 bytes addressed by lane 2 k + (i >> 3), for k = 0..7).
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int vrow = 8 * (s16 >> 3) + 4 * (g16 >> 1) + ((s16 >> 1) & 3);
+  const int vswz = v_swz(vrow);  // rows 64 kc + 16 q + vrow share bits 1..2 with vrow
+  const int v_lane = vrow * ROW8 + 8 * (s16 & 1);
+  const int qq = wave * 32 + m32;
+
+  int j = csr.next(csr.e);
+  wait_vmcnt<0>();  // Q fragments and the CSR chunk are in registers before any tile DMA
+  if (j >= 0) {
+    dma_tile8<false>(Kg, rs, a.S, j * TILE, Ks);
+    dma_tile8<true>(Vg, rs, a.S, j * TILE, Vs);
+  }
+  while (j >= 0) {
+    const int jn = csr.next(csr.e + 1);
+    wait_vmcnt<4>();  // K(j) has landed (V(j) may still be in flight)
+    lds_barrier();
+    // ---- S^T = K Q^T: fragments read one key block ahead ----
+    __builtin_amdgcn_s_setprio(1);
+    f32x16_t s[4];
+    auto read_k = [&](int kb, v8i_t* f) {
+      const char* rowp = Ks + (kb * 32 + m32) * ROW8;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const uint4 c0 = *reinterpret_cast<const uint4*>(rowp + (((4 * kc + 2 * hh) ^ kswz) << 4));
+        const uint4 c1 =
+            *reinterpret_cast<const uint4*>(rowp + (((4 * kc + 2 * hh + 1) ^ kswz) << 4));
+        f[kc] = (v8i_t){(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w,
+                        (int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w};
+      }
+    };
+    v8i_t kf[2][2];
+    read_k(0, kf[0]);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      if (kb < 3) read_k(kb + 1, kf[(kb + 1) & 1]);
+      s[kb] = mfma_fp8(kf[kb & 1][0], qf[0], (f32x16_t){});
+      s[kb] = mfma_fp8(kf[kb & 1][1], qf[1], s[kb]);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    lds_barrier();  // every wave is done with Ks
+    if (jn >= 0) dma_tile8<false>(Kg, rs, a.S, jn * TILE, Ks);
+    // ---- online softmax (base 2) ----
+    if (j == u.qt) {
+      // causal mask inside the diagonal tile; t is made opaque so that the
+      // per-element predicates are not hoisted out of the tile loop
+      int t = qq - 4 * hh;
+      asm volatile("" : "+v"(t));
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + (r & 3) > t) s[kb][r] = -INFINITY;
+    }
+    // The running max comes from the row's first tile; later tiles keep it
+    // while the lane's share of the row sum stays <= 2^8 (so every P <= 256,
+    // inside e4m3's range; the test also catches inf and NaN), else the max
+    // is raised to the tile's and O rescaled, after which every P <= 1.
+    auto tile_max = [&]() {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      return pair_max(mx) * scale_log2;
+    };
+    if (first) {
+      m_run = tile_max();
+      first = false;
+    }
+    // P in e4m3, packed as the B operand of the P.V products: byte j of
+    // dword w of key block kb is the lane's score element r = 4 w + j.
+    int pk[4][4];
+    auto exps = [&]() {
+      const float neg = -m_run;
+      float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w], scale_log2, neg));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w + 1], scale_log2, neg));
+          const float p2 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w + 2], scale_log2, neg));
+          const float p3 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w + 3], scale_log2, neg));
+          int x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+          x = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
+          pk[kb][w] = x;
+          ls0 += p0 + p1;
+          ls1 += p2 + p3;
+        }
+      return ls0 + ls1;
+    };
+    float ls = exps();
+    if (__ballot(!(ls <= 0x1p8f))) {
+      const float m_new = fmaxf(m_run, tile_max());
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      ls = exps();
+    }
+    l_run += ls;
+    if (jn >= 0) wait_vmcnt<4>(); else wait_vmcnt<0>();  // V(j) has landed
+    lds_barrier();
+    // ---- O^T += V^T P^T: fragments read one step ahead ----
+    __builtin_amdgcn_s_setprio(2);
+    auto read_v = [&](int kc, int db, v8i_t& f) {
+      const char* vb = Vs + v_lane + (((2 * db + (g16 & 1)) ^ vswz) << 4) + kc * 64 * ROW8;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v2i_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(vb + 16 * q * ROW8));
+        f[2 * q] = x[0];
+        f[2 * q + 1] = x[1];
+      }
+    };
+    v8i_t vf[2];
+    read_v(0, 0, vf[0]);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const int kc = st >> 2, db = st & 3;
+      if (st < 7) read_v((st + 1) >> 2, (st + 1) & 3, vf[(st + 1) & 1]);
+      const v8i_t b = {pk[2 * kc][0], pk[2 * kc][1], pk[2 * kc][2], pk[2 * kc][3],
+                       pk[2 * kc + 1][0], pk[2 * kc + 1][1], pk[2 * kc + 1][2], pk[2 * kc + 1][3]};
+      o[db] = mfma_fp8(vf[st & 1], b, o[db]);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    lds_barrier();  // every wave is done with Vs
+    if (jn >= 0) dma_tile8<true>(Vg, rs, a.S, jn * TILE, Vs);
+    j = jn;
+  }
+  store_out(static_cast<uint16_t*>(a.out), a.lse, a.S, a.Hq, u.h, u.qt, 0, o, m_run, l_run,
+            out_scale);
+}
+
+}  // namespace
+
+rbs_status launch_attn_fp8_csr(const AttnArgs& a, float q_descale, float k_descale,
+                               float v_descale, hipStream_t st) {
+  const float scale_log2 = a.scale * q_descale * k_descale * 1.4426950408889634f;
+  const int nq = (a.S + TILE - 1) / TILE;
+  hipLaunchKernelGGL(attn_fp8_kernel, dim3(attn_grid(a.Hq, a.Hkv, nq, 1)), dim3(kThreads), 0, st, a,
+                     a.row_ptr, a.col_idx, scale_log2, v_descale);
+  return launch_status();
+}
+
+}  // namespace rbs

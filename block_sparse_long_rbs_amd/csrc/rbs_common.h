@@ -83,6 +83,9 @@ struct AttnArgs {
   int per_head;   // CSR rows per query head (h * nb + i) instead of per KV head (g * nb + i)
 };
 rbs_status launch_attn_bf16_csr(const AttnArgs& a, hipStream_t st);
+// fp8 (e4m3) Q, K, V with per-tensor dequantisation factors; bf16 output.
+rbs_status launch_attn_fp8_csr(const AttnArgs& a, float q_descale, float k_descale,
+                               float v_descale, hipStream_t st);
 // Vector-ALU path: fp32 inputs, or bf16 with head dim or block 64.
 rbs_status launch_attn_vec_csr(const AttnArgs& a, bool bf16, hipStream_t st);
 int select_rows_per_group(int nb, int D);

@@ -4,7 +4,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from .inputs import Workload, to_bf16_bits
+from .inputs import Fp8Inputs, Workload, to_bf16_bits
 
 
 def tensor(x: np.ndarray, dtype: str, device) -> torch.Tensor:
@@ -22,3 +22,10 @@ def upload(w: Workload, device="cuda") -> dict:
     if w.beta is not None:
         out["beta"] = torch.from_numpy(np.ascontiguousarray(w.beta, np.float32)).to(device)
     return out
+
+
+def upload_fp8(f: Fp8Inputs, device="cuda") -> dict:
+    """q, k, v as float8_e4m3fn device tensors (the bytes as given)."""
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.uint8)).to(device).view(  # noqa: E731
+        torch.float8_e4m3fn)
+    return {"q": up(f.q), "k": up(f.k), "v": up(f.v)}

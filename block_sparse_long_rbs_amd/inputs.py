@@ -25,6 +25,9 @@ Workload recipes (named by what they are):
 * ``mixture_bf16_128k`` 131,072 tokens, 32/4 heads, the same key mixture.
 * ``rag_bf16_31k``      Block-attention RAG layout: 20 passages of 1,536
   tokens plus a 512-token final block, 32/8 heads, dim 128, RoPE theta 5e5.
+
+``fp8_inputs`` turns any workload into fp8 (E4M3) Q, K, V with one
+dequantisation factor per tensor, the way an fp8 checkpoint stores them.
 """
 from __future__ import annotations
 
@@ -32,6 +35,41 @@ import dataclasses
 from typing import Optional
 
 import numpy as np
+
+
+@dataclasses.dataclass
+class Fp8Inputs:
+    """fp8 copies of a workload's Q, K, V as an fp8 checkpoint stores them:
+    OCP E4M3 bytes (uint8, same shapes) and one dequantisation factor per
+    tensor (real value = descale * decoded byte)."""
+
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    q_descale: float
+    k_descale: float
+    v_descale: float
+
+
+def to_e4m3(x: np.ndarray):
+    """Per-tensor fp8 quantisation: scale so that the largest magnitude maps
+    to 448 (E4M3's largest finite value), round to nearest even with torch's
+    float8_e4m3fn conversion. Returns (uint8 bytes, float32 descale)."""
+    import torch  # host-side conversion only
+
+    x = np.ascontiguousarray(x, np.float32)
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    descale = np.float32(amax / 448.0) if amax > 0 else np.float32(1.0)
+    scaled = torch.from_numpy(x / descale)
+    return scaled.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy(), float(descale)
+
+
+def fp8_inputs(w: "Workload") -> Fp8Inputs:
+    """E4M3 copies of w.q, w.k, w.v with per-tensor descales."""
+    q, qd = to_e4m3(w.q)
+    k, kd = to_e4m3(w.k)
+    v, vd = to_e4m3(w.v)
+    return Fp8Inputs(q, k, v, qd, kd, vd)
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
@@ -297,3 +335,25 @@ WORKLOADS = {
     "mixture_bf16_128k": mixture_bf16_128k,
     "rag_bf16_31k": rag_bf16_31k,
 }
+
+
+def random_block_csr(n_kv_heads: int, n_blocks: int, density: float, seed: int = 0,
+                     sink: bool = True):
+    """Seeded block lists in rbs_select's CSR form (row g * nb + i, ascending
+    block indices in 0..i, the diagonal always present, block 0 too when
+    sink): each earlier block is drawn with probability `density`. A stand-in
+    selection for attention-only tests; it computes nothing of the method.
+    Returns (row_ptr int64 [Hkv*nb+1], col_idx int32)."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for _ in range(n_kv_heads):
+        for i in range(n_blocks):
+            pick = np.flatnonzero(rng.random(i) < density) if i else np.zeros(0, np.int64)
+            blocks = set(pick.tolist()) | {i}
+            if sink:
+                blocks.add(0)
+            rows.append(sorted(blocks))
+    row_ptr = np.zeros(len(rows) + 1, np.int64)
+    row_ptr[1:] = np.cumsum([len(r) for r in rows])
+    col_idx = np.fromiter((b for r in rows for b in r), np.int32, count=int(row_ptr[-1]))
+    return row_ptr, col_idx

@@ -201,6 +201,33 @@ rbs_status blocksparse_attn_fwd_per_head(rbs_dtype dt, const void* q, const void
                                          void* stream);
 
 /*
+ * blocksparse_attn_fwd_fp8 - blocksparse_attn_fwd with fp8 Q, K and V.
+ *
+ * [RBS] "Integration with vLLM and Benchmark Results": the model the method is
+ * measured on stores its weights in fp8. q, k and v hold OCP E4M3 bytes (sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits; largest finite value 448;
+ * 0x7F and 0xFF are NaN) with one dequantisation factor per tensor: the real
+ * inputs are q_descale * q, k_descale * k and v_descale * v. The result is
+ * blocksparse_attn_fwd's definition on those real inputs (same CSR rows,
+ * causal masking, softmax_scale and lse); out is bf16 [S][Hq][D], rounded to
+ * nearest even.
+ * Arithmetic: Q.K^T as fp8 x fp8 matrix-core products summed in fp32; softmax
+ * in fp32; the probabilities are rounded to E4M3 (nearest even, relative
+ * error <= 2^-4) for the P.V product, summed in fp32. Hence
+ * |out - exact| <= 2^-4 * max over the row's keys of |v_descale * v[u] - out|
+ * up to fp32 and bf16 rounding.
+ * Supported: head_dim 128 and block 128 (else RBS_E_UNSUPPORTED); group CSR
+ * rows g * nb + i as rbs_select writes them.
+ * Errors: RBS_E_ARG (also for a descale that is not finite and > 0),
+ *   RBS_E_UNSUPPORTED, RBS_E_HIP.
+ */
+rbs_status blocksparse_attn_fwd_fp8(const void* q, const void* k, const void* v, int32_t seqlen,
+                                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                    int32_t block, const int32_t* row_ptr, const int32_t* col_idx,
+                                    float softmax_scale, float q_descale, float k_descale,
+                                    float v_descale, void* out, float* lse, void* stream);
+
+/*
  * block_mask_attn_fwd - Block-attention prefill with position re-encoding.
  *
  * [BA] sections 1 and 2.1 "Main Idea": the input is split into blocks whose

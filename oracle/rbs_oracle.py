@@ -332,6 +332,43 @@ def blocksparse_attention(q, k, v, block: int, row_ptr, col_idx, scale: Optional
     return out, lse
 
 
+def e4m3_decode(b) -> np.ndarray:
+    """Real values of fp8 E4M3 bytes, float64, exact.
+
+    Format definition: the OCP 8-bit floating point specification's E4M3
+    (not from the pages; [RBS] "Integration with vLLM and Benchmark Results"
+    only says the evaluated model is an FP8 checkpoint). Bit 7 is the sign,
+    bits 6..3 the exponent e with bias 7, bits 2..0 the mantissa m: e > 0
+    gives (1 + m/8) * 2^(e - 7), e = 0 the subnormal (m/8) * 2^-6; the two
+    codes with every exponent and mantissa bit set (0x7F, 0xFF) are NaN and
+    there is no infinity, so the largest finite value is 448 (0x7E).
+    """
+    b = np.asarray(b, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(F64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(F64) - 7.0))
+    return np.where((b & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def blocksparse_attention_fp8(q8, k8, v8, q_descale: float, k_descale: float, v_descale: float,
+                              block: int, row_ptr, col_idx, scale: Optional[float] = None,
+                              rows: Optional[Iterable] = None):
+    """blocksparse_attention on fp8 inputs: the real inputs are the decoded
+    E4M3 bytes times one dequantisation factor per tensor (q_descale * q,
+    k_descale * k, v_descale * v); everything after that is
+    blocksparse_attention's definition, in float64.
+
+    q8, k8, v8: uint8 arrays of E4M3 bytes, [S, Hq, D] and [S, Hkv, D].
+    """
+    lut = e4m3_decode(np.arange(256))   # every code once; indexing applies it elementwise
+    q = lut[np.asarray(q8, np.uint8)]
+    q *= float(q_descale)
+    k = lut[np.asarray(k8, np.uint8)] * float(k_descale)
+    v = lut[np.asarray(v8, np.uint8)] * float(v_descale)
+    return blocksparse_attention(q, k, v, block, row_ptr, col_idx, scale, rows)
+
+
 def blocksparse_attention_per_head(q, k, v, block: int, row_ptr, col_idx,
                                    scale: Optional[float] = None, rows: Optional[Iterable] = None):
     """Causal GQA attention over per-query-head block lists: query token t in

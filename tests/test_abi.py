@@ -192,3 +192,25 @@ def test_per_head_entry_points_validate_before_launch(L):
     assert r == E.RBS_E_UNSUPPORTED
     r = L.blocksparse_attn_fwd_per_head(0, P, P, P, 0, 8, 2, 128, 128, P, P, 0.0, P, None, None)
     assert r == E.RBS_OK
+
+
+def attn8(L, **kw):
+    a = dict(q=P, k=P, v=P, S=1024, Hq=8, Hkv=2, D=128, B=128, rp=P, ci=P, sc=0.0, qd=1.0, kd=1.0,
+             vd=1.0, o=P, lse=None)
+    a.update(kw)
+    return L.blocksparse_attn_fwd_fp8(a["q"], a["k"], a["v"], a["S"], a["Hq"], a["Hkv"], a["D"],
+                                      a["B"], a["rp"], a["ci"], a["sc"], a["qd"], a["kd"], a["vd"],
+                                      a["o"], a["lse"], None)
+
+
+def test_fp8_attention_validation(L):
+    assert attn8(L, q=None) == E.RBS_E_ARG
+    assert attn8(L, o=PM) == E.RBS_E_ARG
+    assert attn8(L, Hq=10, Hkv=4) == E.RBS_E_ARG
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert attn8(L, qd=bad) == E.RBS_E_ARG
+        assert attn8(L, kd=bad) == E.RBS_E_ARG
+        assert attn8(L, vd=bad) == E.RBS_E_ARG
+    assert attn8(L, D=64, B=128) == E.RBS_E_UNSUPPORTED   # head dim 128 only
+    assert attn8(L, D=128, B=64) == E.RBS_E_UNSUPPORTED   # block 128 only
+    assert attn8(L, S=0) == E.RBS_OK

@@ -361,6 +361,86 @@ def test_per_head_keep_ratio_one_is_dense_causal_attention():
     np.testing.assert_allclose(out, _sdpa_causal(w.q, w.k, w.v), atol=1e-12, rtol=0)
 
 
+# ---------------------------------------------------------------- fp8 (E4M3) inputs
+
+def test_e4m3_decode_matches_torch_on_every_code():
+    """The decoder written from the format definition against torch's own
+    float8_e4m3fn conversion, all 256 byte values (NaN codes included)."""
+    b = np.arange(256, dtype=np.uint8)
+    mine = orc.e4m3_decode(b)
+    ref = torch.from_numpy(b.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    same = (mine == ref) | (np.isnan(mine) & np.isnan(ref))
+    assert same.all(), b[~same]
+
+
+def test_e4m3_closed_forms():
+    d = lambda x: float(orc.e4m3_decode(np.array([x], np.uint8))[0])  # noqa: E731
+    assert d(0x38) == 1.0 and d(0xB8) == -1.0          # exponent field 7 = bias
+    assert d(0x7E) == 448.0                            # largest finite: 1.75 * 2^8
+    assert d(0x08) == 2.0 ** -6                        # smallest normal
+    assert d(0x01) == 2.0 ** -9 and d(0x07) == 7 * 2.0 ** -9   # subnormals m/8 * 2^-6
+    assert d(0x00) == 0.0 and math.copysign(1.0, d(0x80)) == -1.0
+    assert math.isnan(d(0x7F)) and math.isnan(d(0xFF))
+    pos = orc.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)                    # codes 0..0x7E increase strictly
+
+
+def _fp8_case(S=200, Hq=4, Hkv=2, D=16, B=32, seed=4):
+    w = inputs.mixture_small(S=S, Hq=Hq, Hkv=Hkv, D=D, B=B, rho=0.3, sink=True, seed=seed)
+    f = inputs.fp8_inputs(w)
+    c, r, qr, qn = orc.block_stats(w.q, w.k, Hkv, B)
+    sel = orc.select(c, r, qr, qn, orc.derive_beta(r), 0.3, 0.3, sink=True)
+    return w, f, sel
+
+
+def test_fp8_attention_equals_token_level_brute_force():
+    """Decoded-and-scaled inputs through the token-mask attention (a separate
+    code path) give the same result."""
+    w, f, sel = _fp8_case()
+    out, lse = orc.blocksparse_attention_fp8(f.q, f.k, f.v, f.q_descale, f.k_descale,
+                                             f.v_descale, 32, sel.row_ptr, sel.col_idx)
+    mask = orc.csr_token_mask(sel.row_ptr, sel.col_idx, 2, 200, 32)
+    q = orc.e4m3_decode(f.q) * f.q_descale
+    k = orc.e4m3_decode(f.k) * f.k_descale
+    v = orc.e4m3_decode(f.v) * f.v_descale
+    out2, lse2 = orc.masked_attention(q, k, v, mask)
+    np.testing.assert_allclose(out, out2, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse, lse2, atol=1e-12, rtol=0)
+
+
+def test_fp8_descales_act_as_the_definition_says():
+    """v_descale scales the output; q_descale and k_descale enter only through
+    their product with the softmax scale (a swapped or dropped factor fails)."""
+    w, f, sel = _fp8_case()
+    base, lse = orc.blocksparse_attention_fp8(f.q, f.k, f.v, 1.0, 1.0, 1.0, 32, sel.row_ptr,
+                                              sel.col_idx, scale=0.25)
+    o2, l2 = orc.blocksparse_attention_fp8(f.q, f.k, f.v, 1.0, 1.0, 3.0, 32, sel.row_ptr,
+                                           sel.col_idx, scale=0.25)
+    np.testing.assert_allclose(o2, 3.0 * base, rtol=1e-13, atol=0)
+    np.testing.assert_allclose(l2, lse, rtol=0, atol=1e-13)
+    o3, l3 = orc.blocksparse_attention_fp8(f.q, f.k, f.v, 2.0, 0.5, 1.0, 32, sel.row_ptr,
+                                           sel.col_idx, scale=0.25)
+    np.testing.assert_allclose(o3, base, rtol=0, atol=1e-13)
+    o4, l4 = orc.blocksparse_attention_fp8(f.q, f.k, f.v, 2.0, 1.0, 1.0, 32, sel.row_ptr,
+                                           sel.col_idx, scale=0.125)
+    np.testing.assert_allclose(o4, base, rtol=0, atol=1e-13)
+    o5, _ = orc.blocksparse_attention_fp8(f.q, f.k, f.v, 2.0, 1.0, 1.0, 32, sel.row_ptr,
+                                          sel.col_idx, scale=0.25)
+    assert np.abs(o5 - base).max() > 1e-3        # the product really matters
+
+
+def test_fp8_inputs_round_trip():
+    """The generator's quantisation is a rounding: decoded values are within
+    half a step (2^-4 relative, 2^-10 absolute below 2^-6) of the scaled input."""
+    w = inputs.random_qkv(300, 2, 1, 32, "f32", seed=3, block=64)
+    b, d = inputs.to_e4m3(w.q)
+    x = w.q.astype(np.float64) / d
+    y = orc.e4m3_decode(b)
+    assert np.abs(x).max() <= 448.0 * (1 + 1e-6) and np.isfinite(y).all()   # descale is fp32-rounded
+    err = np.abs(y - x)
+    assert np.all(err <= np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10) + 1e-12)
+
+
 # ---------------------------------------------------------------- Block-attention
 
 def test_rope_composition():
