@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 matrix-core peak (256 CU x 2.4 GHz x 4096 flop/clk)
+FP8_PEAK_TFLOPS = 5033.2       # MI355X dense fp8 matrix-core peak (256 CU x 2.4 GHz x 8192 flop/clk)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 METRIC = "block-sparse prefill attn ms/layer + effective TFLOP/s (% bf16 peak) at 128K"
 
@@ -259,6 +260,29 @@ def main():
         log(f"per-query-head selection: stats {ph[0]:.3f} select {ph[1]:.3f} attn {ph[2]:.3f} ms "
             f"({flops_h / (ph[2] * 1e-3) / 1e12:.1f} TFLOP/s, {int(rph[-1])} CSR entries)")
         del wsh, outh
+        # fp8 (E4M3) Q, K, V with per-tensor descales, on the same block lists
+        f8 = inputs.fp8_inputs(w)
+        t8 = device.upload_fp8(f8)
+        fp8_args = (t8["q"], t8["k"], t8["v"], B, rp, ci, f8.q_descale, f8.k_descale,
+                    f8.v_descale)
+        for _ in range(3):
+            rbs.blocksparse_attn_fwd_fp8(*fp8_args, out=out)
+        e0.record(stream)
+        for _ in range(10):
+            rbs.blocksparse_attn_fwd_fp8(*fp8_args, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_f8 = e0.elapsed_time(e1) / 10
+        tf_f8 = flops / (t_f8 * 1e-3) / 1e12
+        result["fp8_e4m3_attention"] = {
+            "attn_ms": round(t_f8, 4), "tflops": round(tf_f8, 1),
+            "frac_of_fp8_peak": round(tf_f8 / FP8_PEAK_TFLOPS, 4),
+            "fp8_peak_tflops": FP8_PEAK_TFLOPS,
+            "speedup_over_bf16": round(t_attn / t_f8, 3),
+            "inputs": "the bf16 workload quantised per tensor to E4M3 (largest magnitude -> 448)"}
+        log(f"fp8 attention {t_f8:.3f} ms, {tf_f8:.1f} TFLOP/s "
+            f"({tf_f8 / FP8_PEAK_TFLOPS * 100:.1f}% of the fp8 peak)")
+        del f8, t8, fp8_args
         # Block-attention RAG workload
         wr = inputs.rag_bf16_31k()
         tr = device.upload(wr)
