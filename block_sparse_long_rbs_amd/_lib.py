@@ -117,12 +117,44 @@ def _need_cuda(*ts):
             raise ValueError("tensors must be contiguous and on the GPU")
 
 
+# Host-side shape checks: the kernels trust the sizes passed with the
+# pointers, so every tensor is checked against them before a call.
+
+def _check_qkv(fn: str, q, k, v=None):
+    if q.dim() != 3 or k.dim() != 3 or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2]:
+        raise ValueError(f"{fn}: q must be [S, Hq, D] and k [S, Hkv, D], got {tuple(q.shape)} "
+                         f"and {tuple(k.shape)}")
+    if v is not None and v.shape != k.shape:
+        raise ValueError(f"{fn}: v must have k's shape {tuple(k.shape)}, got {tuple(v.shape)}")
+    for t in (k, v):
+        if t is not None and (t.dtype != q.dtype or t.device != q.device):
+            raise TypeError(f"{fn}: q, k and v must share dtype and device")
+
+
+def _check_tensor(fn: str, name: str, t, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device:
+        raise ValueError(f"{fn}: {name} must be {dtype} {tuple(shape)} on {device}, got "
+                         f"{t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def _check_csr(fn: str, row_ptr, col_idx, n_rows: int, device):
+    _check_tensor(fn, "row_ptr", row_ptr, (n_rows + 1,), torch.int32, device)
+    if col_idx.dim() != 1 or col_idx.dtype != torch.int32 or col_idx.device != device:
+        raise ValueError(f"{fn}: col_idx must be a 1-D int32 tensor on {device} (holding at "
+                         "least row_ptr[-1] entries)")
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
 # ---------------------------------------------------------------------------
 
 def rbs_block_stats(q: torch.Tensor, k: torch.Tensor, block: int):
     """Per-block centroid, radius, representative query and its norm.
     q [S, Hq, D], k [S, Hkv, D] (bf16 or f32) -> fp32 (cen [Hkv,nb,D],
     rad [Hkv,nb], q_rep [Hkv,nb,D], q_rep_norm [Hkv,nb])."""
+    _check_qkv("rbs_block_stats", q, k)
     _need_cuda(q, k)
     S, Hq, D = q.shape
     Hkv = k.shape[1]
@@ -140,6 +172,7 @@ def rbs_block_stats_per_head(q: torch.Tensor, k: torch.Tensor, block: int):
     """Centroid and radius per KV head, representative query per query head:
     -> fp32 (cen [Hkv,nb,D], rad [Hkv,nb], q_rep_head [Hq,nb,D],
     q_rep_head_norm [Hq,nb])."""
+    _check_qkv("rbs_block_stats_per_head", q, k)
     _need_cuda(q, k)
     S, Hq, D = q.shape
     Hkv = k.shape[1]
@@ -165,21 +198,27 @@ def rbs_select(cen, rad, qrep, qnorm, keep_ratio_centroid: float, keep_ratio_res
     """Dual-branch selection -> (row_ptr [Hkv*nb+1] int32, col_idx [capacity]
     int32, beta_used [Hkv,nb] fp32 or None). Only col_idx[:row_ptr[-1]] is
     meaningful."""
-    _need_cuda(cen, rad, qrep, qnorm, beta)
     Hkv, nb, D = cen.shape
+    dev = cen.device
+    for name, t, shape in (("cen", cen, (Hkv, nb, D)), ("rad", rad, (Hkv, nb)),
+                           ("qrep", qrep, (Hkv, nb, D)), ("qnorm", qnorm, (Hkv, nb)),
+                           ("beta", beta, (Hkv, nb))):
+        if t is not None:
+            _check_tensor("rbs_select", name, t, shape, torch.float32, dev)
+    _need_cuda(cen, rad, qrep, qnorm, beta)
     flags = RBS_SEL_FORCE_SINK if sink else 0
     L = lib()
     ws = ctypes.c_size_t(0)
     _check("rbs_select", L.rbs_select(None, None, None, None, None, Hkv, nb, D,
                                       keep_ratio_centroid, keep_ratio_rescue, flags, None, None,
                                       None, 0, None, ctypes.byref(ws), None))
-    if workspace is None or workspace.numel() < ws.value:
+    if workspace is None or _nbytes(workspace) < ws.value:
         workspace = torch.empty(ws.value, dtype=torch.uint8, device=cen.device)
     cap = rbs_select_capacity(Hkv, nb, keep_ratio_centroid, keep_ratio_rescue, sink)
     row_ptr = torch.empty(Hkv * nb + 1, dtype=torch.int32, device=cen.device)
     col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=cen.device)
     beta_out = torch.empty((Hkv, nb), dtype=torch.float32, device=cen.device) if want_beta else None
-    wsz = ctypes.c_size_t(workspace.numel())
+    wsz = ctypes.c_size_t(_nbytes(workspace))
     _check("rbs_select", L.rbs_select(
         cen.data_ptr(), rad.data_ptr(), qrep.data_ptr(), qnorm.data_ptr(), _ptr(beta), Hkv, nb, D,
         keep_ratio_centroid, keep_ratio_rescue, flags, _ptr(beta_out), row_ptr.data_ptr(),
@@ -193,22 +232,28 @@ def rbs_select_per_head(cen, rad, qrep_head, qnorm_head, keep_ratio_centroid: fl
                         workspace: Optional[torch.Tensor] = None):
     """Per-query-head selection -> (row_ptr [Hq*nb+1] int32, col_idx int32,
     beta_used [Hkv,nb] fp32 or None); rows h * nb + i."""
-    _need_cuda(cen, rad, qrep_head, qnorm_head, beta)
     Hkv, nb, D = cen.shape
     Hq = qrep_head.shape[0]
+    dev = cen.device
+    for name, t, shape in (("cen", cen, (Hkv, nb, D)), ("rad", rad, (Hkv, nb)),
+                           ("qrep_head", qrep_head, (Hq, nb, D)), ("qnorm_head", qnorm_head, (Hq, nb)),
+                           ("beta", beta, (Hkv, nb))):
+        if t is not None:
+            _check_tensor("rbs_select_per_head", name, t, shape, torch.float32, dev)
+    _need_cuda(cen, rad, qrep_head, qnorm_head, beta)
     flags = RBS_SEL_FORCE_SINK if sink else 0
     L = lib()
     ws = ctypes.c_size_t(0)
     _check("rbs_select_per_head", L.rbs_select_per_head(
         None, None, None, None, None, Hq, Hkv, nb, D, keep_ratio_centroid, keep_ratio_rescue,
         flags, None, None, None, 0, None, ctypes.byref(ws), None))
-    if workspace is None or workspace.numel() < ws.value:
+    if workspace is None or _nbytes(workspace) < ws.value:
         workspace = torch.empty(ws.value, dtype=torch.uint8, device=cen.device)
     cap = rbs_select_capacity(Hq, nb, keep_ratio_centroid, keep_ratio_rescue, sink)
     row_ptr = torch.empty(Hq * nb + 1, dtype=torch.int32, device=cen.device)
     col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=cen.device)
     beta_out = torch.empty((Hkv, nb), dtype=torch.float32, device=cen.device) if want_beta else None
-    wsz = ctypes.c_size_t(workspace.numel())
+    wsz = ctypes.c_size_t(_nbytes(workspace))
     _check("rbs_select_per_head", L.rbs_select_per_head(
         cen.data_ptr(), rad.data_ptr(), qrep_head.data_ptr(), qnorm_head.data_ptr(), _ptr(beta),
         Hq, Hkv, nb, D, keep_ratio_centroid, keep_ratio_rescue, flags, _ptr(beta_out),
@@ -221,9 +266,14 @@ def blocksparse_attn_fwd_per_head(q, k, v, block: int, row_ptr, col_idx,
                                   softmax_scale: float = 0.0, want_lse: bool = False,
                                   out: Optional[torch.Tensor] = None):
     """Causal GQA attention over per-query-head CSR block lists (row h * nb + i)."""
-    _need_cuda(q, k, v, row_ptr, col_idx)
+    fn = "blocksparse_attn_fwd_per_head"
+    _check_qkv(fn, q, k, v)
     S, Hq, D = q.shape
     Hkv = k.shape[1]
+    _check_csr(fn, row_ptr, col_idx, Hq * -(-S // block), q.device)
+    if out is not None:
+        _check_tensor(fn, "out", out, q.shape, q.dtype, q.device)
+    _need_cuda(q, k, v, row_ptr, col_idx, out)
     if out is None:
         out = torch.empty_like(q)
     lse = torch.empty((Hq, S), dtype=torch.float32, device=q.device) if want_lse else None
@@ -237,9 +287,14 @@ def blocksparse_attn_fwd_per_head(q, k, v, block: int, row_ptr, col_idx,
 def blocksparse_attn_fwd(q, k, v, block: int, row_ptr, col_idx, softmax_scale: float = 0.0,
                          want_lse: bool = False, out: Optional[torch.Tensor] = None):
     """Causal GQA attention over the CSR-selected key blocks -> (out, lse or None)."""
-    _need_cuda(q, k, v, row_ptr, col_idx)
+    fn = "blocksparse_attn_fwd"
+    _check_qkv(fn, q, k, v)
     S, Hq, D = q.shape
     Hkv = k.shape[1]
+    _check_csr(fn, row_ptr, col_idx, Hkv * -(-S // block), q.device)
+    if out is not None:
+        _check_tensor(fn, "out", out, q.shape, q.dtype, q.device)
+    _need_cuda(q, k, v, row_ptr, col_idx, out)
     if out is None:
         out = torch.empty_like(q)
     lse = torch.empty((Hq, S), dtype=torch.float32, device=q.device) if want_lse else None
@@ -256,12 +311,16 @@ def blocksparse_attn_fwd_fp8(q, k, v, block: int, row_ptr, col_idx, q_descale: f
                              out: Optional[torch.Tensor] = None):
     """blocksparse_attn_fwd on fp8 (torch.float8_e4m3fn) Q, K, V with per-tensor
     dequantisation factors -> (bf16 out, lse or None)."""
-    _need_cuda(q, k, v, row_ptr, col_idx)
-    for t in (q, k, v):
-        if t.dtype != torch.float8_e4m3fn:
-            raise TypeError(f"blocksparse_attn_fwd_fp8 takes float8_e4m3fn tensors, got {t.dtype}")
+    fn = "blocksparse_attn_fwd_fp8"
+    if q.dtype != torch.float8_e4m3fn:
+        raise TypeError(f"{fn} takes float8_e4m3fn tensors, got {q.dtype}")
+    _check_qkv(fn, q, k, v)
     S, Hq, D = q.shape
     Hkv = k.shape[1]
+    _check_csr(fn, row_ptr, col_idx, Hkv * -(-S // block), q.device)
+    if out is not None:
+        _check_tensor(fn, "out", out, q.shape, torch.bfloat16, q.device)
+    _need_cuda(q, k, v, row_ptr, col_idx, out)
     if out is None:
         out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=q.device)
     lse = torch.empty((Hq, S), dtype=torch.float32, device=q.device) if want_lse else None
@@ -303,8 +362,12 @@ def block_mask_attn_fwd(q, k_cached, v, seg_start: Sequence[int], k_rerotate: Se
     """Block-attention prefill with RoPE re-encoding of cached keys -> (out, lse or None).
     The workspace (re-encoded keys; partial results of the final block's split
     rows) is allocated when not given or too small."""
-    _need_cuda(q, k_cached, v)
+    fn = "block_mask_attn_fwd"
+    _check_qkv(fn, q, k_cached, v)
     S, Hq, D = q.shape
+    if out is not None:
+        _check_tensor(fn, "out", out, q.shape, q.dtype, q.device)
+    _need_cuda(q, k_cached, v, out)
     if out is None:
         out = torch.empty_like(q)
     lse = torch.empty((Hq, S), dtype=torch.float32, device=q.device) if want_lse else None
@@ -312,9 +375,9 @@ def block_mask_attn_fwd(q, k_cached, v, seg_start: Sequence[int], k_rerotate: Se
                        softmax_scale, out, lse)
     need = ctypes.c_size_t(0)
     _check("block_mask_attn_fwd", lib().block_mask_attn_fwd(*args, None, ctypes.byref(need), None))
-    if workspace is None or workspace.numel() < max(need.value, 1):
+    if workspace is None or _nbytes(workspace) < max(need.value, 1):
         workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
-    wsz = ctypes.c_size_t(workspace.numel())
+    wsz = ctypes.c_size_t(_nbytes(workspace))
     _check("block_mask_attn_fwd", lib().block_mask_attn_fwd(
         *args, workspace.data_ptr(), ctypes.byref(wsz), _stream(q)))
     return out, lse
