@@ -342,10 +342,13 @@ def counted_traffic():
     import hashlib
     import re
     path = os.path.join(ROOT, "profiles", "attn_bf16_csr_mixture_128k_pmc.md")
-    src = os.path.join(ROOT, "block_sparse_long_rbs_amd", "csrc", "attn_bf16.hip")
+    csrc = os.path.join(ROOT, "block_sparse_long_rbs_amd", "csrc")
     try:
         text = open(path).read()
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        h = hashlib.sha256()
+        for name in ("attn_bf16.hip", "attn_tiles.h"):   # the kernel's sources, in this order
+            h.update(open(os.path.join(csrc, name), "rb").read())
+        sha = h.hexdigest()
     except OSError:
         return None
     m = re.search(r"source_sha256: ([0-9a-f]{64}).*?hbm_bytes_per_launch: (\d+)", text, re.S)
