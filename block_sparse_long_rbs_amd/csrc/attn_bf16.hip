@@ -50,48 +50,6 @@ constexpr int ROWB = D * 2;          // bytes per K or V row in LDS
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-// Normalised output tile through LDS (buf: 32 KB, free when called): each
-// lane writes its 4-value groups of O/l as bf16 into its row (16-byte chunks
-// swizzled by row, as for K), then each wave reads back its own 32 rows as
-// whole 16-byte chunks, so that the stores to O cover 256 contiguous bytes
-// per row instead of 8 bytes of 64 different rows. Only the wave's own rows
-// are touched: no workgroup barrier.
-__device__ __forceinline__ void store_out_lds(uint16_t* __restrict__ O, float* __restrict__ lse,
-                                              int S, int Hq, int h, int qt, int row_begin,
-                                              const f32x16_t* o, float m_run, float l_run,
-                                              char* buf) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int m32 = lane & 31, hh = lane >> 5;
-  const float l = pair_sum(l_run);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  {
-    const int r = wave * 32 + m32;
-    char* rowp = buf + r * ROWB;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int chunk = db * 4 + rg;  // 8 head dims from db * 32 + 8 rg; this lane's 4 at + 4 hh
-        const uint2 v = make_uint2(cvt_pk_bf16(o[db][4 * rg] * inv, o[db][4 * rg + 1] * inv),
-                                   cvt_pk_bf16(o[db][4 * rg + 2] * inv, o[db][4 * rg + 3] * inv));
-        *reinterpret_cast<uint2*>(rowp + ((chunk ^ (r & 15)) << 4) + 8 * hh) = v;
-      }
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
-  __builtin_amdgcn_wave_barrier();
-  const int t_lse = qt * TILE + wave * 32 + m32;
-  if (lse && hh == 0 && t_lse < S && t_lse >= row_begin)
-    lse[(size_t)h * S + t_lse] = l > 0.f ? (m_run + __log2f(l)) * 0.69314718055994530942f : -INFINITY;
-#pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int r = wave * 32 + it * 4 + (lane >> 4), chunk = lane & 15;
-    const uint4 v = *reinterpret_cast<const uint4*>(buf + r * ROWB + ((chunk ^ (r & 15)) << 4));
-    const int t = qt * TILE + r;
-    if (t < S && t >= row_begin)
-      *reinterpret_cast<uint4*>(O + ((size_t)t * Hq + h) * D + chunk * 8) = v;
-  }
-}
-
 // 16-byte chunk swizzles in LDS: chunk c of K row r sits at slot c ^ (r & 15)
 // (fragments read 16 rows x one chunk), chunk c of V row r at c ^ ((r & 3) << 2)
 // (transposing reads take 4 rows x four chunks).
@@ -446,7 +404,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
                o, m_run, l_run);
   else
     store_out_lds(static_cast<uint16_t*>(a.out), a.lse, a.S, a.Hq, u.h, u.qt,
-                  SEG ? seg.q_row_begin : 0, o, m_run, l_run, Ks);
+                  SEG ? seg.q_row_begin : 0, o, m_run, l_run, 1.0f, Ks);
 }
 
 }  // namespace

@@ -114,8 +114,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_kernel(AttnArgs a,
                                                                const int32_t* __restrict__ row_ptr,
                                                                const int32_t* __restrict__ col_idx,
                                                                float scale_log2, float out_scale) {
-  __shared__ __attribute__((aligned(1024))) char Ks[TILE * ROW8];
-  __shared__ __attribute__((aligned(1024))) char Vs[TILE * ROW8];
+  // K and V tiles side by side: together they stage the 32 KB output tile
+  __shared__ __attribute__((aligned(1024))) char KVs[2 * TILE * ROW8];
+  char* const Ks = KVs;
+  char* const Vs = KVs + TILE * ROW8;
   __shared__ int lst[kThreads];
   const int G = a.Hq / a.Hkv;
   const int nq = (a.S + TILE - 1) / TILE;
@@ -285,8 +287,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_kernel(AttnArgs a,
     if (jn >= 0) dma_tile8<true>(Vg, rs, a.S, jn * TILE, Vs);
     j = jn;
   }
-  store_out(static_cast<uint16_t*>(a.out), a.lse, a.S, a.Hq, u.h, u.qt, 0, o, m_run, l_run,
-            out_scale);
+  store_out_lds(static_cast<uint16_t*>(a.out), a.lse, a.S, a.Hq, u.h, u.qt, 0, o, m_run, l_run,
+                out_scale, KVs);
 }
 
 }  // namespace

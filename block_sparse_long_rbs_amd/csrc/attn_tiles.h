@@ -93,30 +93,48 @@ __device__ __forceinline__ bool decode_unit(int x, int G, int Hkv, int qt_lo, in
 }
 
 // Normalised output of one query tile (bf16, O / l times out_scale) and the
-// row's log-sum-exp (natural log; -inf for a row that saw no key).
-__device__ __forceinline__ void store_out(uint16_t* __restrict__ O, float* __restrict__ lse, int S,
-                                          int Hq, int h, int qt, int row_begin, const f32x16_t* o,
-                                          float m_run, float l_run, float out_scale) {
+// row's log-sum-exp (natural log; -inf for a row that saw no key), through
+// LDS (buf: 32 KB, 16-byte aligned, free when called): each lane writes its
+// 4-value groups into its row (16-byte chunks swizzled by row), then each
+// wave reads back its own 32 rows as whole 16-byte chunks, so that the stores
+// to O cover 256 contiguous bytes per row instead of 8 bytes of 64 different
+// rows. Only the wave's own rows are touched: no workgroup barrier.
+__device__ __forceinline__ void store_out_lds(uint16_t* __restrict__ O, float* __restrict__ lse,
+                                              int S, int Hq, int h, int qt, int row_begin,
+                                              const f32x16_t* o, float m_run, float l_run,
+                                              float out_scale, char* buf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m32 = lane & 31, hh = lane >> 5;
-  const int t = qt * TILE + wave * 32 + m32;
   const float l = pair_sum(l_run);
-  if (t >= S || t < row_begin) return;
   const float inv = l > 0.f ? out_scale / l : 0.f;
-  uint16_t* orow = O + ((size_t)t * Hq + h) * D;
+  constexpr int kRowBytes = D * 2;  // one bf16 output row
+  {
+    const int r = wave * 32 + m32;
+    char* rowp = buf + r * kRowBytes;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int d = db * 32 + 8 * rg + 4 * hh;
-      const uint2 v = make_uint2(cvt_pk_bf16(o[db][4 * rg] * inv, o[db][4 * rg + 1] * inv),
-                                 cvt_pk_bf16(o[db][4 * rg + 2] * inv, o[db][4 * rg + 3] * inv));
-      *reinterpret_cast<uint2*>(orow + d) = v;
-    }
-  if (lse && hh == 0)
-    lse[(size_t)h * S + t] = l > 0.f ? (m_run + __log2f(l)) * 0.69314718055994530942f : -INFINITY;
+      for (int rg = 0; rg < 4; ++rg) {
+        const int chunk = db * 4 + rg;  // 8 head dims from db * 32 + 8 rg; this lane's 4 at + 4 hh
+        const uint2 v = make_uint2(cvt_pk_bf16(o[db][4 * rg] * inv, o[db][4 * rg + 1] * inv),
+                                   cvt_pk_bf16(o[db][4 * rg + 2] * inv, o[db][4 * rg + 3] * inv));
+        *reinterpret_cast<uint2*>(rowp + ((chunk ^ (r & 15)) << 4) + 8 * hh) = v;
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  const int t_lse = qt * TILE + wave * 32 + m32;
+  if (lse && hh == 0 && t_lse < S && t_lse >= row_begin)
+    lse[(size_t)h * S + t_lse] = l > 0.f ? (m_run + __log2f(l)) * 0.69314718055994530942f : -INFINITY;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int r = wave * 32 + it * 4 + (lane >> 4), chunk = lane & 15;
+    const uint4 v = *reinterpret_cast<const uint4*>(buf + r * kRowBytes + ((chunk ^ (r & 15)) << 4));
+    const int t = qt * TILE + r;
+    if (t < S && t >= row_begin)
+      *reinterpret_cast<uint4*>(O + ((size_t)t * Hq + h) * D + chunk * 8) = v;
+  }
 }
-
 
 // Key tiles of one unit in CSR mode: the row's block list, staged in LDS 256
 // entries at a time (a vector load inside the tile loop would make every wait
