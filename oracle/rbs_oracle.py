@@ -369,6 +369,35 @@ def blocksparse_attention_fp8(q8, k8, v8, q_descale: float, k_descale: float, v_
     return blocksparse_attention(q, k, v, block, row_ptr, col_idx, scale, rows)
 
 
+def block_attention_mass(q, k, block: int, g: int, i: int, scale: Optional[float] = None):
+    """Dense causal attention mass per key block for one (KV head g, query
+    block i) row: for every query token t of block i and query head h of
+    group g, p_u = softmax_u(scale * q[t][h] . k[u][g]) over the keys u <= t;
+    the mass of key block j is the sum of p_u over its tokens, averaged over
+    the row's tokens and heads. Returns float64 [i + 1] (sums to 1).
+
+    [RBS] "The Standard Approach and Its Blind Spot": a block's importance is
+    the attention it actually receives; the selectors only estimate it.
+    READING: scale defaults to 1/sqrt(D).
+    """
+    S, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
+    t0, t1 = _block_range(i, block, S)
+    qi = q[t0:t1, g * G:(g + 1) * G].astype(F64).transpose(1, 0, 2)   # [G, L, D]
+    kk = k[:t1, g].astype(F64)                                          # [t1, D]
+    logits = (qi @ kk.T) * scale                                        # [G, L, t1]
+    tok = np.arange(t0, t1)
+    logits[:, np.arange(t1)[None, :] > tok[:, None]] = -np.inf
+    logits -= logits.max(axis=-1, keepdims=True)
+    p = np.exp(logits)
+    p /= p.sum(axis=-1, keepdims=True)
+    per_key = p.mean(axis=(0, 1))                                       # [t1]
+    edges = np.arange(0, t1, block)
+    return np.add.reduceat(per_key, edges)
+
+
 def blocksparse_attention_per_head(q, k, v, block: int, row_ptr, col_idx,
                                    scale: Optional[float] = None, rows: Optional[Iterable] = None):
     """Causal GQA attention over per-query-head block lists: query token t in

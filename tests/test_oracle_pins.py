@@ -361,6 +361,29 @@ def test_per_head_keep_ratio_one_is_dense_causal_attention():
     np.testing.assert_allclose(out, _sdpa_causal(w.q, w.k, w.v), atol=1e-12, rtol=0)
 
 
+# ---------------------------------------------------------------- attention mass per block
+
+def test_block_attention_mass_against_library_softmax():
+    """Per-block mass with block size 1 is the per-key softmax (scipy),
+    averaged over the row's tokens and heads; with any block size it sums to
+    1 and equals the per-key masses summed over each block."""
+    from scipy.special import softmax
+    w = inputs.random_qkv(96, 4, 2, 16, "f32", seed=21, block=32)
+    g, i = 1, 2
+    m1 = orc.block_attention_mass(w.q, w.k, 1, g, 70)   # one "block" = one token, row t = 70
+    ref = np.zeros(71)
+    for h in (2, 3):
+        ref += softmax(w.k[:71, g].astype(float) @ w.q[70, h].astype(float) / 4.0)
+    np.testing.assert_allclose(m1, ref / 2, atol=1e-13, rtol=0)
+    m = orc.block_attention_mass(w.q, w.k, 32, g, i)
+    assert m.shape == (3,) and abs(m.sum() - 1.0) < 1e-12
+    per_tok = np.zeros(96)
+    for t in range(64, 96):
+        per_tok[:t + 1] += orc.block_attention_mass(w.q, w.k, 1, g, t)[:t + 1] / 32
+    np.testing.assert_allclose(m, [per_tok[0:32].sum(), per_tok[32:64].sum(), per_tok[64:96].sum()],
+                               atol=1e-12, rtol=0)
+
+
 # ---------------------------------------------------------------- fp8 (E4M3) inputs
 
 def test_e4m3_decode_matches_torch_on_every_code():
