@@ -6,23 +6,30 @@
 // standard block-sparse attention; this is that attention for fp8 caches.
 //
 // Work decomposition, CSR iteration, online softmax and XCD-aware grid are
-// those of the bf16 kernel (attn_bf16.hip). Per key tile:
+// those of the bf16 kernel (attn_bf16.hip). Per key tile, in two 64-key
+// halves (only one half's scores are live at a time):
 //   S^T = K Q^T: per 32-key block, two products of depth 64. A lane holds 32
-//     consecutive head-dim bytes of its key row (two 16-byte LDS reads) and
-//     of its query row (registers). The MFMA pairs A and B bytes by the same
-//     (lane half, byte) position, so one common byte order serves both.
+//     consecutive head-dim bytes of its key row and of its query row, both
+//     read from LDS (two 16-byte reads each). The MFMA pairs A and B bytes by
+//     the same (lane half, byte) position, so one common byte order serves
+//     both.
 //   P = 2^(s - m) rounded to e4m3 (nearest even) straight from the score
 //     registers. e4m3 tops out at 448 and has no infinity (larger values
 //     become NaN), so the running max is raised as soon as a lane's share of
-//     a tile's row sum exceeds 2^8: every P stays <= 256.
-//   O^T += V^T P^T: per 32-wide slice of the head dim and 64-key chunk, one
+//     a half's row sum exceeds 2^8: every P stays <= 256.
+//   O^T += V^T P^T: per 32-wide slice of the head dim and 64-key half, one
 //     product. The V^T operand comes from 8-bit transposing LDS reads
 //     (ds_read_b64_tr_b8), ordered so that byte j of a lane pairs with the
 //     key that byte j of the P operand holds.
 // Scores are scaled by softmax_scale * q_descale * k_descale, the output by
-// v_descale. K and V tiles are 16 KB each (128 bytes per key row), moved HBM
+// v_descale. Q, K and V tiles are 16 KB each (128 bytes per row), moved HBM
 // -> LDS by global_load_lds_dwordx4 with explicit vector-memory counts as in
 // the bf16 kernel (4 loads per wave per tile instead of 8).
+//
+// The softmax's vector instructions, not the matrix products, set the pace,
+// and one wave issues them at a fraction of the SIMD's rate; so the kernel is
+// held to 168 VGPRs (half-tile scores, Q read from LDS) and 49 KB of LDS,
+// which lets three workgroups share a CU (three waves per SIMD).
 //
 // Bound: matrix cores. Algorithmic flops per (query row, key) pair: 4*D.
 
@@ -61,7 +68,11 @@ __device__ __forceinline__ int v_swz(int r) { return ((r >> 1) & 3) << 1; }
 template <bool IS_V>
 __device__ __forceinline__ void dma_tile8(const uint8_t* __restrict__ src, size_t rs, int S,
                                           int key0, char* lds) {
-  const int lane = threadIdx.x & 63;
+  // the lane's offsets are recomputed at every call from an opaque copy of
+  // the thread id, so that none of them has to stay live across the tile loop
+  uint32_t tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r8 = lane >> 3, pc = lane & 7;
   const uint32_t dst = lds_u32(lds) + wave * 4 * 1024;
@@ -89,33 +100,13 @@ __device__ __forceinline__ void dma_tile8(const uint8_t* __restrict__ src, size_
   }
 }
 
-// Q fragments of one query tile: for depth chunk kc (head dims 64 kc ..
-// 64 kc + 63), lane l holds bytes 64 kc + 32 (l >> 5) .. + 31 of its query
-// row. Rows past the end are zero.
-__device__ __forceinline__ void load_q8(const uint8_t* __restrict__ Q, int S, int Hq, int h, int qt,
-                                        v8i_t* qf) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = qt * TILE + wave * 32 + (lane & 31);
-  const int hh = lane >> 5;
-#pragma unroll
-  for (int kc = 0; kc < 2; ++kc) {
-    uint4 u0 = make_uint4(0, 0, 0, 0), u1 = make_uint4(0, 0, 0, 0);
-    if (t < S) {
-      const uint8_t* p = Q + ((size_t)t * Hq + h) * D + 64 * kc + 32 * hh;
-      u0 = *reinterpret_cast<const uint4*>(p);
-      u1 = *reinterpret_cast<const uint4*>(p + 16);
-    }
-    qf[kc] = (v8i_t){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
-                     (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-  }
-}
-
-__global__ __launch_bounds__(kThreads, 2) void attn_fp8_kernel(AttnArgs a,
+__global__ __launch_bounds__(kThreads, 3) void attn_fp8_kernel(AttnArgs a,
                                                                const int32_t* __restrict__ row_ptr,
                                                                const int32_t* __restrict__ col_idx,
                                                                float scale_log2, float out_scale) {
   // K and V tiles side by side: together they stage the 32 KB output tile
   __shared__ __attribute__((aligned(1024))) char KVs[2 * TILE * ROW8];
+  __shared__ __attribute__((aligned(1024))) char Qs[TILE * ROW8];
   char* const Ks = KVs;
   char* const Vs = KVs + TILE * ROW8;
   __shared__ int lst[kThreads];
@@ -139,8 +130,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_kernel(AttnArgs a,
     lds_barrier();
   }
 
-  v8i_t qf[2];
-  load_q8(static_cast<const uint8_t*>(a.q), a.S, a.Hq, u.h, u.qt, qf);
   f32x16_t o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = (f32x16_t){};
@@ -162,93 +151,97 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_kernel(AttnArgs a,
   const int qq = wave * 32 + m32;
 
   int j = csr.next(csr.e);
-  wait_vmcnt<0>();  // Q fragments and the CSR chunk are in registers before any tile DMA
+  wait_vmcnt<0>();  // the CSR chunk is in registers before any tile DMA
   if (j >= 0) {
+    // the query tile is staged like a K tile (same swizzle); rows past the
+    // end repeat the last row and their outputs are never stored
+    dma_tile8<false>(static_cast<const uint8_t*>(a.q) + (size_t)u.h * D, (size_t)a.Hq * D, a.S,
+                     u.qt * TILE, Qs);
     dma_tile8<false>(Kg, rs, a.S, j * TILE, Ks);
     dma_tile8<true>(Vg, rs, a.S, j * TILE, Vs);
   }
+  // 16-byte LDS reads of a fragment: chunks 4 kc + 2 hh and 4 kc + 2 hh + 1
+  // of a row stored with the K swizzle (query rows and key rows alike)
+  auto read_frag = [&](const char* rowp, int kc) {
+    const uint4 c0 = *reinterpret_cast<const uint4*>(rowp + (((4 * kc + 2 * hh) ^ kswz) << 4));
+    const uint4 c1 = *reinterpret_cast<const uint4*>(rowp + (((4 * kc + 2 * hh + 1) ^ kswz) << 4));
+    return (v8i_t){(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w,
+                   (int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w};
+  };
+  const char* const qrow = Qs + qq * ROW8;
+  const char* const krow = Ks + m32 * ROW8;
   while (j >= 0) {
     const int jn = csr.next(csr.e + 1);
-    wait_vmcnt<4>();  // K(j) has landed (V(j) may still be in flight)
+    wait_vmcnt<4>();  // K(j) (and at the first tile Q) has landed; V(j) may be in flight
     lds_barrier();
-    // ---- S^T = K Q^T: fragments read one key block ahead ----
-    __builtin_amdgcn_s_setprio(1);
-    f32x16_t s[4];
-    auto read_k = [&](int kb, v8i_t* f) {
-      const char* rowp = Ks + (kb * 32 + m32) * ROW8;
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const uint4 c0 = *reinterpret_cast<const uint4*>(rowp + (((4 * kc + 2 * hh) ^ kswz) << 4));
-        const uint4 c1 =
-            *reinterpret_cast<const uint4*>(rowp + (((4 * kc + 2 * hh + 1) ^ kswz) << 4));
-        f[kc] = (v8i_t){(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w,
-                        (int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w};
-      }
-    };
-    v8i_t kf[2][2];
-    read_k(0, kf[0]);
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      if (kb < 3) read_k(kb + 1, kf[(kb + 1) & 1]);
-      s[kb] = mfma_fp8(kf[kb & 1][0], qf[0], (f32x16_t){});
-      s[kb] = mfma_fp8(kf[kb & 1][1], qf[1], s[kb]);
-    }
-    __builtin_amdgcn_s_setprio(0);
-    lds_barrier();  // every wave is done with Ks
-    if (jn >= 0) dma_tile8<false>(Kg, rs, a.S, jn * TILE, Ks);
-    // ---- online softmax (base 2) ----
-    if (j == u.qt) {
-      // causal mask inside the diagonal tile; t is made opaque so that the
-      // per-element predicates are not hoisted out of the tile loop
-      int t = qq - 4 * hh;
-      asm volatile("" : "+v"(t));
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kb * 32 + 8 * (r >> 2) + (r & 3) > t) s[kb][r] = -INFINITY;
-    }
-    // The running max comes from the row's first tile; later tiles keep it
-    // while the lane's share of the row sum stays <= 2^8 (so every P <= 256,
-    // inside e4m3's range; the test also catches inf and NaN), else the max
-    // is raised to the tile's and O rescaled, after which every P <= 1.
-    auto tile_max = [&]() {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      return pair_max(mx) * scale_log2;
-    };
-    if (first) {
-      m_run = tile_max();
-      first = false;
-    }
+    const bool diag = j == u.qt;
+    // causal mask inside the diagonal tile; t is made opaque so that the
+    // per-element predicates are not hoisted out of the tile loop
+    int t = qq - 4 * hh;
+    asm volatile("" : "+v"(t));
     // P in e4m3, packed as the B operand of the P.V products: byte j of
     // dword w of key block kb is the lane's score element r = 4 w + j.
     int pk[4][4];
-    auto exps = [&]() {
-      const float neg = -m_run;
-      float ls0 = 0.f, ls1 = 0.f;
+    float ls[2];
+    f32x16_t s[2];
+    // S^T = K Q^T for the 64-key half `half` (key blocks 2 half, 2 half + 1),
+    // in the order (depth chunk, key block) so that one Q fragment is live
+    auto scores = [&](int half) {
+      __builtin_amdgcn_s_setprio(1);
+      v8i_t kf = read_frag(krow + (2 * half) * 32 * ROW8, 0);
+      v8i_t qc = read_frag(qrow, 0);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int x = 0; x < 4; ++x) {
+        const int kc = x >> 1, kk = x & 1;
+        const v8i_t cur = kf;
+        if (x < 3) kf = read_frag(krow + (2 * half + ((x + 1) & 1)) * 32 * ROW8, (x + 1) >> 1);
+        s[kk] = mfma_fp8(cur, qc, kc ? s[kk] : (f32x16_t){});
+        if (x == 1) qc = read_frag(qrow, 1);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      if (diag) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if ((2 * half + kk) * 32 + 8 * (r >> 2) + (r & 3) > t) s[kk][r] = -INFINITY;
+      }
+    };
+    auto half_max = [&]() {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kk][r]);
+      return pair_max(mx) * scale_log2;
+    };
+    auto exps = [&](int half) {
+      const float neg = -m_run;
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w], scale_log2, neg));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w + 1], scale_log2, neg));
-          const float p2 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w + 2], scale_log2, neg));
-          const float p3 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * w + 3], scale_log2, neg));
-          int x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-          x = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
-          pk[kb][w] = x;
-          ls0 += p0 + p1;
-          ls1 += p2 + p3;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kk][4 * w], scale_log2, neg));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kk][4 * w + 1], scale_log2, neg));
+          const float p2 = __builtin_amdgcn_exp2f(fmaf(s[kk][4 * w + 2], scale_log2, neg));
+          const float p3 = __builtin_amdgcn_exp2f(fmaf(s[kk][4 * w + 3], scale_log2, neg));
+          int xw = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+          xw = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, xw, true);
+          pk[2 * half + kk][w] = xw;
+          a0 += p0 + p1;
+          a1 += p2 + p3;
         }
-      return ls0 + ls1;
+      ls[half] = a0 + a1;
     };
-    float ls = exps();
-    if (__ballot(!(ls <= 0x1p8f))) {
-      const float m_new = fmaxf(m_run, tile_max());
+    // The running max comes from the row's first half tile. It stays while a
+    // lane's share of a half's row sum is <= 2^8 (every P <= 256, inside
+    // e4m3's range; the test also catches inf and NaN); else it is raised to
+    // that half's max and O and the row sum are rescaled. A raise in the
+    // second half recomputes the first half from K, still in LDS, so every P
+    // is rounded once, from its exact exponential.
+    auto raise = [&]() {
+      const float m_new = fmaxf(m_run, half_max());
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
@@ -256,9 +249,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_kernel(AttnArgs a,
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      ls = exps();
+    };
+    scores(0);
+    if (first) {
+      m_run = half_max();
+      first = false;
     }
-    l_run += ls;
+    exps(0);
+    if (__ballot(!(ls[0] <= 0x1p8f))) {
+      raise();
+      exps(0);
+    }
+    scores(1);
+    exps(1);
+    if (__ballot(!(ls[1] <= 0x1p8f))) {
+      raise();
+      exps(1);
+      scores(0);
+      exps(0);
+    }
+    lds_barrier();  // every wave is done with Ks
+    if (jn >= 0) dma_tile8<false>(Kg, rs, a.S, jn * TILE, Ks);
+    l_run += ls[0] + ls[1];
     if (jn >= 0) wait_vmcnt<4>(); else wait_vmcnt<0>();  // V(j) has landed
     lds_barrier();
     // ---- O^T += V^T P^T: fragments read one step ahead ----

@@ -128,6 +128,41 @@ def test_fp8_late_dominant_key_raises_the_running_max():
     _compare(w, f, out_g, lse_g, out_o, lse_o, [(0, i) for i in range(4)], "fp8 late key")
 
 
+def test_fp8_raise_in_second_half_recomputes_first_half():
+    """Every query is 4*e0, so a key's base-2 score is b = 4 k0 scale log2(e)
+    and is set by its first coordinate alone. Keys default to b = 0, which
+    fixes the running max at 0 from the first tile. In tile 2, key 300 (first
+    64-key half) sits at b ~ 3, so the first half keeps the max (a lane's
+    share of its row sum is about 8 + 31 < 2^8). Keys 320..383 (second half)
+    sit at b = 4, so every lane's share of the second half's row sum is
+    32 * 16 > 2^8. Rows that see them therefore raise the max in the second
+    half, and the first half's P, already packed, has to be redone from the
+    new max. Every kept probability stays in e4m3's normal range."""
+    w = inputs.random_qkv(512, 2, 1, 128, "f32", seed=11, block=128)
+    unit = 1.0 / (4.0 / math.sqrt(128) * math.log2(math.e))  # k0 for b = 1
+    q = np.zeros_like(w.q)
+    q[:, :, 0] = 4.0
+    k = w.k.copy()
+    k[:, :, 0] = 0.0
+    k[300, 0, 0] = 3.0 * unit
+    k[320:384, 0, 0] = 4.0 * unit
+    w.q, w.k = q, k
+    H.say("[case] fp8 raise in the second half S=512")
+    f = inputs.fp8_inputs(w)
+    # the construction survives quantisation
+    qd = orc.e4m3_decode(f.q[:, 0]) * f.q_descale
+    kd = orc.e4m3_decode(f.k[:, 0]) * f.k_descale
+    b = kd @ qd[400] / math.sqrt(128) * math.log2(math.e)
+    assert np.all(b[:300] == 0) and np.all(b[301:320] == 0) and np.all(b[384:] == 0)
+    assert 2.5 < b[300] < 3.5 and np.allclose(b[320:384], 4.0, atol=1e-6)
+    row_ptr, col_idx = orc.dense_causal_selection(1, 4)
+    t = device.upload_fp8(f)
+    out_g, lse_g = _run(f, t, 128, row_ptr, col_idx)
+    out_o, lse_o = orc.blocksparse_attention_fp8(f.q, f.k, f.v, f.q_descale, f.k_descale,
+                                                 f.v_descale, 128, row_ptr, col_idx)
+    _compare(w, f, out_g, lse_g, out_o, lse_o, [(0, i) for i in range(4)], "fp8 second-half raise")
+
+
 @pytest.mark.timeout(600)
 def test_fp8_128k_sampled_rows():
     """131,072 tokens, 32/4 heads, the 128K key mixture in fp8, seeded block
