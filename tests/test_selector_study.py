@@ -94,3 +94,54 @@ def test_mixture_128k_rescue_branch_keeps_more_mass():
     res = _study(w, _sample(np.random.default_rng(2), 4, 256, w.n_blocks, 6))
     assert res["ret_dual"].mean() > res["ret_cen"].mean()
     assert res["top_share"][4] >= 0.5
+
+
+def _needle_recall(w, needles):
+    """For planted needles (KV head g, key block b, query block i that its key
+    is aligned with): how many blocks b each branch keeps in row (g, i), with
+    beta = 1 (the full Cauchy-Schwarz margin for every block) and with the
+    derived beta. Returns {name: (centroid, rescue, union)} hit counts."""
+    c, r, qr, qn = orc.block_stats(w.q, w.k, w.n_kv_heads, w.block)
+    res = {}
+    for name, beta in (("beta=1", np.ones_like(r)), ("derived beta", orc.derive_beta(r))):
+        hits = np.zeros(3, int)
+        for g, b, i in needles:
+            sc, sr = orc.branch_scores(c, r, qr, qn, beta, g, i)
+            pc = set(orc.top_n(sc.astype(np.float32), orc.budget(i + 1, w.keep_ratio_centroid)).tolist())
+            pr = set(orc.top_n(sr.astype(np.float32), orc.budget(i + 1, w.keep_ratio_rescue)).tolist())
+            hits += [b in pc, b in pr, b in (pc | pr)]
+        res[name] = tuple(int(x) for x in hits)
+    return res
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_needle_recall_tiny_f32_1k(seed):
+    """Diagnostic, printed with -s. The 1K workload plants four needle blocks
+    whose one aligned key sits among keys pushed away from the query direction,
+    so their centroid scores are the lowest and their radii large. Whether the
+    rescue branch finds them depends on beta: with beta = 1 every block gets
+    its full Cauchy-Schwarz margin and the isotropic blocks' margins (large
+    radius too) crowd the needles out; the derived beta gives the margin only
+    to blocks whose radius is well above the head's mean. Recall is reported,
+    not asserted: it is a property of the recipe, not of the selector."""
+    w = inputs.tiny_f32_1k(seed=seed)
+    i = w.recipe["query_block"]
+    needles = [(0, int(b), i) for b in w.recipe["needle_blocks"]]
+    res = _needle_recall(w, needles)
+    print(f"\n{w.name} seed {seed}: needle blocks kept in row {i} (of {len(needles)}), "
+          + "; ".join(f"{k}: centroid {v[0]}, rescue {v[1]}, union {v[2]}" for k, v in res.items()))
+    for hc, hr, hu in res.values():
+        assert max(hc, hr) <= hu <= hc + hr
+
+
+def test_needle_recall_needle_bf16_8k():
+    """Diagnostic, printed with -s: the 8K workload's planted needles (one key
+    of norm 6 along the group's mean query direction of a later query block,
+    among N(0,1) keys), kept by each branch in that query block's row."""
+    w = inputs.needle_bf16_8k()
+    needles = [(g, b, i) for g, b, i, _ in w.recipe["needles"]]
+    res = _needle_recall(w, needles)
+    print(f"\n{w.name}: needle blocks kept (of {len(needles)}), "
+          + "; ".join(f"{k}: centroid {v[0]}, rescue {v[1]}, union {v[2]}" for k, v in res.items()))
+    for hc, hr, hu in res.values():
+        assert max(hc, hr) <= hu <= hc + hr
