@@ -121,6 +121,18 @@ def test_cauchy_schwarz_bound_exhaustive_8k():
     assert _cs_check(inputs.needle_bf16_8k()) <= 1e-12
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("make", [inputs.mixture_bf16_32k, inputs.mixture_bf16_128k],
+                         ids=["32k", "128k"])
+def test_cauchy_schwarz_bound_sampled_mixtures(make):
+    """The same bound on sampled query blocks of the two mixtures (every KV
+    head, every key block up to the diagonal), including the last block."""
+    w = make()
+    rng = np.random.default_rng(0)
+    rows = sorted(rng.choice(w.n_blocks - 1, size=5, replace=False).tolist()) + [w.n_blocks - 1]
+    assert _cs_check(w, rows) <= 1e-12
+
+
 def test_cauchy_schwarz_tight_for_aligned_outlier():
     """A block whose farthest key is aligned with q reaches the bound."""
     rng = np.random.default_rng(5)
