@@ -71,6 +71,21 @@ def test_fp8_ragged_small_all_rows():
     _compare(w, f, out_g, lse_g, out_o, lse_o, rows, "fp8 attention")
 
 
+def test_fp8_last_tile_shorter_than_a_half():
+    """700 tokens: the last tile holds 60 keys, so its second 64-key half lies
+    wholly past the end (every score masked); 4/1 heads, all rows."""
+    w = inputs.mixture_small(S=700, Hq=4, Hkv=1, seed=6)
+    H.say(f"[case] fp8 short last tile S={w.seqlen}")
+    f = inputs.fp8_inputs(w)
+    _, sel = H.oracle_selection(w)
+    t = device.upload_fp8(f)
+    out_g, lse_g = _run(f, t, w.block, sel.row_ptr, sel.col_idx)
+    out_o, lse_o = orc.blocksparse_attention_fp8(f.q, f.k, f.v, f.q_descale, f.k_descale,
+                                                 f.v_descale, w.block, sel.row_ptr, sel.col_idx)
+    rows = [(g, i) for g in range(w.n_kv_heads) for i in range(w.n_blocks)]
+    _compare(w, f, out_g, lse_g, out_o, lse_o, rows, "fp8 short last tile")
+
+
 def test_fp8_descales_scale_exactly():
     """Doubling v_descale doubles every output bit for bit; moving a factor 2
     from k_descale to q_descale changes nothing."""
