@@ -41,7 +41,8 @@ extern "C" {
 typedef enum rbs_status {
   RBS_OK = 0,
   RBS_E_ARG = 1,          /* null pointer, bad size, misalignment, bad ratio, bad segments */
-  RBS_E_UNSUPPORTED = 2,  /* valid but not implemented: dtype/head_dim/block combination, sizes */
+  RBS_E_UNSUPPORTED = 2,  /* valid but not implemented: dtype/head_dim/block combination, sizes
+                             (among them seqlen * n_q_heads * head_dim > 2^40) */
   RBS_E_CAPACITY = 3,     /* col_capacity or workspace too small */
   RBS_E_HIP = 4           /* a HIP runtime call or kernel launch failed */
 } rbs_status;

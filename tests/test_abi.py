@@ -214,3 +214,12 @@ def test_fp8_attention_validation(L):
     assert attn8(L, D=64, B=128) == E.RBS_E_UNSUPPORTED   # head dim 128 only
     assert attn8(L, D=128, B=64) == E.RBS_E_UNSUPPORTED   # block 128 only
     assert attn8(L, S=0) == E.RBS_OK
+
+
+def test_sizes_beyond_the_supported_range_are_refused(L):
+    """A Q (or O) of more than 2^40 elements is refused on the host with
+    RBS_E_UNSUPPORTED, before anything is enqueued."""
+    big = dict(S=2 ** 30, Hq=16, Hkv=2, D=128)          # 2^41 elements in Q
+    assert stats(L, **big) == E.RBS_E_UNSUPPORTED
+    assert attn(L, **big) == E.RBS_E_UNSUPPORTED
+    assert bmask(L, seg=(0, 2 ** 30), rer=(0,), **big) == E.RBS_E_UNSUPPORTED
