@@ -179,6 +179,27 @@ def test_fp8_raise_in_second_half_recomputes_first_half():
 
 
 @pytest.mark.timeout(600)
+def test_fp8_32k_64_8_heads_sampled_rows():
+    """32,768 tokens, 64/8 heads (the 32K mixture's head layout), the oracle's
+    selection, sampled (KV head, query block) rows."""
+    w = inputs.mixture_bf16_32k()
+    H.say(f"[case] fp8 {w.name} S={w.seqlen}")
+    f = inputs.fp8_inputs(w)
+    _, sel = H.oracle_selection(w)
+    t = device.upload_fp8(f)
+    out_g, lse_g = _run(f, t, w.block, sel.row_ptr, sel.col_idx)
+    nb = w.n_blocks
+    rng = np.random.default_rng(4)
+    allrows = [(g, i) for g in range(w.n_kv_heads) for i in range(nb)]
+    pick = rng.choice(len(allrows), size=8, replace=False)
+    rows = [allrows[x] for x in sorted(pick)] + [(0, 0), (w.n_kv_heads - 1, nb - 1)]
+    out_o, lse_o = orc.blocksparse_attention_fp8(f.q, f.k, f.v, f.q_descale, f.k_descale,
+                                                 f.v_descale, w.block, sel.row_ptr, sel.col_idx,
+                                                 rows=rows)
+    _compare(w, f, out_g, lse_g, out_o, lse_o, rows, "fp8 32K sampled rows")
+
+
+@pytest.mark.timeout(600)
 def test_fp8_128k_sampled_rows():
     """131,072 tokens, 32/4 heads, the 128K key mixture in fp8, seeded block
     lists at about the selection's density (6%), the launch the benchmark times;

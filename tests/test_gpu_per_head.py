@@ -81,6 +81,14 @@ def test_per_head_needle_8k_sampled():
     per_head_case(inputs.needle_bf16_8k(), sample_rows=48)
 
 
+@pytest.mark.timeout(600)
+def test_per_head_mixture_128k_sampled():
+    """The benchmarked 128K workload (32/4 heads, keep-ratio 0.03, sink) with
+    one list per query head: statistics and every row's set, attention on
+    sampled (query head, query block) rows."""
+    per_head_case(inputs.mixture_bf16_128k(), sample_rows=10, seed=3)
+
+
 def test_per_head_reps_average_to_the_group_reps_on_gpu():
     """The GPU's per-head representatives average over each group to the
     GPU's group representative (both from their own single pass)."""
