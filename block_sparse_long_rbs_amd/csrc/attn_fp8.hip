@@ -14,9 +14,11 @@
 //     the same (lane half, byte) position, so one common byte order serves
 //     both.
 //   P = 2^(s - m) rounded to e4m3 (nearest even) straight from the score
-//     registers. e4m3 tops out at 448 and has no infinity (larger values
-//     become NaN), so the running max is raised as soon as a lane's share of
-//     a half's row sum exceeds 2^8: every P stays <= 256.
+//     registers; the row sum adds the same rounded values. The reference m
+//     is kept 3 below the largest score seen when it is set (largest P 8),
+//     which keeps small probabilities out of e4m3's subnormal range; e4m3
+//     tops out at 448 and has no infinity (larger values become NaN), so m is
+//     raised as soon as a lane's share of a half's row sum exceeds 448.
 //   O^T += V^T P^T: per 32-wide slice of the head dim and 64-key half, one
 //     product. The V^T operand comes from 8-bit transposing LDS reads
 //     (ds_read_b64_tr_b8), ordered so that byte j of a lane pairs with the
@@ -229,19 +231,30 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fp8_kernel(AttnArgs a,
           int xw = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
           xw = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, xw, true);
           pk[2 * half + kk][w] = xw;
-          a0 += p0 + p1;
-          a1 += p2 + p3;
+          // the row sum adds the rounded P that the P.V product uses, so the
+          // output stays a weighted mean of V (an overflowed P decodes as NaN)
+          const auto r01 = __builtin_amdgcn_cvt_pk_f32_fp8(xw, false);
+          const auto r23 = __builtin_amdgcn_cvt_pk_f32_fp8(xw, true);
+          a0 += r01[0] + r01[1];
+          a1 += r23[0] + r23[1];
         }
       ls[half] = a0 + a1;
     };
-    // The running max comes from the row's first half tile. It stays while a
-    // lane's share of a half's row sum is <= 2^8 (every P <= 256, inside
-    // e4m3's range; the test also catches inf and NaN); else it is raised to
-    // that half's max and O and the row sum are rescaled. A raise in the
-    // second half recomputes the first half from K, still in LDS, so every P
-    // is rounded once, from its exact exponential.
+    // The reference m_run sits kMaxLift below the largest score seen when it
+    // is set, so that the half tile's largest P is 2^kMaxLift rather than 1:
+    // small probabilities then stay clear of e4m3's subnormal range (below
+    // 2^-6) and of its flush to zero (below 2^-10), which would otherwise
+    // drop the mass of a long tail of small P. It is set from the row's
+    // first half tile and stays while a lane's share of a half's row sum of
+    // rounded P is <= 448 (every P finite in e4m3; an overflow decodes as NaN
+    // and fails the test too); else it is raised to that half's max minus
+    // kMaxLift and O and the row sum are rescaled. After a raise every P of
+    // the half is <= 2^kMaxLift, so a lane's 32 values sum to <= 256 and the
+    // test passes. A raise in the second half recomputes the first half from
+    // K, still in LDS, so every P is rounded once, from its exact exponential.
+    constexpr float kMaxLift = 3.f;
     auto raise = [&]() {
-      const float m_new = fmaxf(m_run, half_max());
+      const float m_new = fmaxf(m_run, half_max() - kMaxLift);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
@@ -252,17 +265,17 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fp8_kernel(AttnArgs a,
     };
     scores(0);
     if (first) {
-      m_run = half_max();
+      m_run = half_max() - kMaxLift;
       first = false;
     }
     exps(0);
-    if (__ballot(!(ls[0] <= 0x1p8f))) {
+    if (__ballot(!(ls[0] <= 448.f))) {
       raise();
       exps(0);
     }
     scores(1);
     exps(1);
-    if (__ballot(!(ls[1] <= 0x1p8f))) {
+    if (__ballot(!(ls[1] <= 448.f))) {
       raise();
       exps(1);
       scores(0);

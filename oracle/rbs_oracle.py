@@ -23,9 +23,8 @@ in ``query_rep_per_head``), the rounding of
 the per-branch budget (``budget``), the tie-break (``top_n``) and the RoPE
 pairing style (``rope_rotate``).
 
-Everything is computed in float64 from the given (float32-held) inputs.
-Selection decisions (which scores rank above which) are taken after rounding
-the float64 scores to float32, the precision the GPU kernels rank in.
+Everything is computed in float64 from the given (float32-held) inputs,
+selection decisions included: scores are ranked as float64 numbers.
 """
 from __future__ import annotations
 
@@ -150,12 +149,39 @@ def budget(n_visible: int, keep_ratio: float) -> int:
     return min(n_visible, max(1, math.ceil(float(keep_ratio) * n_visible - 1e-6)))
 
 
-def top_n(scores32: np.ndarray, n: int) -> np.ndarray:
-    """Indices of the n best entries, best = larger score, ties to the lower
-    index (READING: the pages give no tie rule). Returned ascending."""
-    idx = np.arange(scores32.shape[0])
-    order = np.lexsort((idx, -scores32.astype(F64)))
-    return np.sort(order[:n])
+def rank_order(scores: np.ndarray) -> np.ndarray:
+    """Entry indices from best to worst: larger float64 score first, equal
+    scores by lower index (READING: the pages give no tie rule)."""
+    idx = np.arange(scores.shape[0])
+    return np.lexsort((idx, -np.asarray(scores, F64)))
+
+
+def top_n(scores: np.ndarray, n: int) -> np.ndarray:
+    """Indices of the n best entries (see :func:`rank_order`), ascending."""
+    return np.sort(rank_order(scores)[:n])
+
+
+def near_tie_band(scores: np.ndarray, n: int, floor: float, band_rel: float = 1e-4) -> set:
+    """Entries whose membership in one branch's top-n is decided by rounding.
+
+    tau is the n-th best float64 score and the band is every entry within
+    band_rel * max(|tau|, floor) of it (READING: the relative 1e-4 of the
+    parity rule, with floor the natural size of the branch's score terms so
+    that a threshold near zero still has a band). A computation carried out in
+    lower precision can exchange a kept entry for a dropped one only when both
+    lie in the band, so the band counts only when it holds entries on both
+    sides of the cut (at least one kept and one dropped); otherwise it is
+    empty and the n-th entry itself is decided exactly.
+    """
+    s = np.asarray(scores, F64)
+    order = rank_order(s)
+    tau = s[order[n - 1]]
+    near = np.abs(s - tau) <= band_rel * max(abs(tau), floor)
+    kept = np.zeros(s.shape[0], bool)
+    kept[order[:n]] = True
+    if not (near & ~kept).any():
+        return set()
+    return set(np.nonzero(near)[0].tolist())
 
 
 @dataclasses.dataclass
@@ -199,11 +225,12 @@ def select(centroid, radius, q_rep, q_rep_norm, beta, keep_ratio_centroid: float
 
     beta: [Hkv, nb] array (given or from :func:`derive_beta`).
 
-    ``exempt`` marks, per row, non-forced blocks whose float64 score is within
-    band_rel * max(|tau|, floor) of a branch's threshold tau (the budget-th
-    largest float64 score), floor being the size of that branch's score terms:
-    ||q|| * max_j ||c_j|| for the centroid branch and
-    ||q|| * max_j (||c_j|| + r_j * beta_j) for the rescue branch.
+    ``exempt`` marks, per row, the non-forced blocks of each branch's
+    :func:`near_tie_band`, with floor ||q|| * max_j ||c_j|| for the centroid
+    branch and ||q|| * max_j (||c_j|| + r_j * beta_j) for the rescue branch:
+    the only blocks whose membership a lower-precision ranking may decide
+    differently. A branch whose budget-th block has no rival across the cut
+    inside the band exempts nothing.
     """
     Hkv, nb, D = centroid.shape
     beta = np.asarray(beta, F64)
@@ -214,18 +241,15 @@ def select(centroid, radius, q_rep, q_rep_norm, beta, keep_ratio_centroid: float
             sc, sr = branch_scores(centroid, radius, q_rep, q_rep_norm, beta, g, i)
             nc = budget(i + 1, keep_ratio_centroid)
             nr = budget(i + 1, keep_ratio_rescue)
-            keep = set(top_n(sc.astype(np.float32), nc).tolist())
-            keep |= set(top_n(sr.astype(np.float32), nr).tolist())
+            keep = set(top_n(sc, nc).tolist())
+            keep |= set(top_n(sr, nr).tolist())
             forced = {i} | ({0} if sink else set())
             keep |= forced
             rows.append(np.array(sorted(keep), dtype=np.int32))
-            ex = set()
-            for s, n, floor in ((sc, nc, q_rep_norm[g, i] * cnorm[g, :i + 1].max()),
-                                (sr, nr, q_rep_norm[g, i] *
-                                 (cnorm[g, :i + 1] + radius[g, :i + 1] * beta[g, :i + 1]).max())):
-                tau = np.sort(s)[::-1][n - 1]
-                band = band_rel * max(abs(tau), floor)
-                ex |= set(np.nonzero(np.abs(s - tau) <= band)[0].tolist())
+            floor_c = q_rep_norm[g, i] * cnorm[g, :i + 1].max()
+            floor_r = q_rep_norm[g, i] * (cnorm[g, :i + 1] +
+                                          radius[g, :i + 1] * beta[g, :i + 1]).max()
+            ex = near_tie_band(sc, nc, floor_c, band_rel) | near_tie_band(sr, nr, floor_r, band_rel)
             exempt.append(ex - forced)
     counts = np.array([len(r) for r in rows], dtype=np.int64)
     row_ptr = np.zeros(Hkv * nb + 1, np.int64)

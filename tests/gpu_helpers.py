@@ -51,10 +51,20 @@ def compare_stats(gpu, ora, rel=1e-5):
         assert err <= rel * max(scale, 1e-30), f"{name}: max err {err} vs scale {scale}"
 
 
-def compare_selection(sel, rp_h, ci_h, Hkv, nb, sink):
-    """Sets bit-exact except blocks in the oracle's threshold band. Returns
-    (rows that differ, rows checked)."""
+# At most this share of rows may differ from the oracle at all (every
+# difference must also lie in a near-tie band): float32 scoring should flip
+# a near tie only now and then.
+MAX_DIFF_ROW_FRAC = 0.01
+
+
+def compare_selection(sel, rp_h, ci_h, Hkv, nb, sink, max_diff_frac=MAX_DIFF_ROW_FRAC):
+    """Sets bit-exact except blocks in a near-tie band of the oracle (a band
+    that straddles a branch's cut, see oracle.near_tie_band); the rows that
+    differ at all are capped at max_diff_frac of the rows. Returns (rows that
+    differ, rows checked, exempt blocks)."""
     differing = 0
+    n_exempt = sum(len(e) for e in sel.exempt)
+    assert len(rp_h) == Hkv * nb + 1 and rp_h[0] == 0, "row_ptr has the wrong length or start"
     for r in range(Hkv * nb):
         i = r % nb
         got = ci_h[rp_h[r]:rp_h[r + 1]].tolist()
@@ -68,7 +78,9 @@ def compare_selection(sel, rp_h, ci_h, Hkv, nb, sink):
             differing += 1
             assert diff <= sel.exempt[r], (f"row {r}: differs at {sorted(diff)}, "
                                            f"exempt {sorted(sel.exempt[r])}")
-    return differing, Hkv * nb
+    cap = max(1, int(max_diff_frac * Hkv * nb))
+    assert differing <= cap, f"{differing} of {Hkv * nb} rows differ (cap {cap})"
+    return differing, Hkv * nb, n_exempt
 
 
 def attn_errors(gpu_out, ora_out, rows_tokens, heads=None):
@@ -92,6 +104,41 @@ def check_attn(w, gpu_out, ora_out, tokens):
 def csr_to_device(row_ptr, col_idx, dev="cuda"):
     return (torch.from_numpy(np.asarray(row_ptr, np.int32)).to(dev),
             torch.from_numpy(np.asarray(col_idx, np.int32)).to(dev))
+
+
+def long_rows_csr(n_kv_heads, nb, long_row, n_entries, seed=0):
+    """A CSR whose row `long_row` (of every KV head) lists n_entries entries:
+    every visible block 0..long_row in a shuffled order, with out-of-range
+    entries (-1, long_row + 1, nb + 7) spliced in around list positions 256 and
+    512, where the attention kernels reload their staged block list; every
+    other row holds only its diagonal block. Returns (row_ptr, col_idx) as
+    listed and the clean (row_ptr, col_idx) the oracle reads (the same rows
+    without the out-of-range entries, which attention skips)."""
+    rng = np.random.default_rng(seed)
+    bad = [-1, long_row + 1, nb + 7]
+    rows, clean = [], []
+    for _ in range(n_kv_heads):
+        for i in range(nb):
+            if i != long_row:
+                rows.append([i])
+                clean.append([i])
+                continue
+            good = rng.permutation(long_row + 1).tolist()
+            n_bad = n_entries - len(good)
+            assert n_bad >= 6, "too few entries for the out-of-range splices"
+            lst = list(good)
+            for pos in (254, 255, 256, 257, 511, 512):
+                lst.insert(min(pos, len(lst)), bad[pos % 3])
+            while len(lst) < n_entries:
+                lst.insert(int(rng.integers(len(lst) + 1)), bad[int(rng.integers(3))])
+            rows.append(lst)
+            clean.append(sorted(good))
+
+    def pack(rr):
+        rp = np.zeros(len(rr) + 1, np.int64)
+        np.cumsum([len(x) for x in rr], out=rp[1:])
+        return rp, np.concatenate([np.asarray(x, np.int32) for x in rr])
+    return pack(rows), pack(clean)
 
 
 def row_tokens(rows, block, S):
@@ -125,6 +172,24 @@ def _assert_attn(w, mx, mean, what):
         assert mx <= TOL_BF16_MAX and mean <= TOL_BF16_MEAN, f"{what}: max {mx} mean {mean}"
 
 
+def stratified_rows(n_heads, nb, row_ptr, n, seed=0):
+    """About n (head, query block) rows for a sampled check: for every head
+    its first and last query block and its two longest rows (by the given
+    CSR), then random other rows; sorted."""
+    lengths = np.diff(np.asarray(row_ptr, np.int64)).reshape(n_heads, nb)
+    pick = set()
+    for h in range(n_heads):
+        pick |= {(h, 0), (h, nb - 1)}
+        for i in np.argsort(-lengths[h], kind="stable")[:2]:
+            pick.add((h, int(i)))
+    rng = np.random.default_rng(seed)
+    total = n_heads * nb
+    while len(pick) < min(n, total):
+        r = int(rng.integers(total))
+        pick.add((r // nb, r % nb))
+    return sorted(pick)
+
+
 def pipeline_case(w, sample_rows=None, seed=0):
     """Full parity for one workload; sample_rows bounds the attention oracle."""
     say(f"[case] {w.name} S={w.seqlen} Hq={w.n_q_heads} Hkv={w.n_kv_heads} D={w.head_dim} "
@@ -139,13 +204,12 @@ def pipeline_case(w, sample_rows=None, seed=0):
     if w.beta is None:
         np.testing.assert_allclose(beta_g, sel.beta, atol=1e-5)
     nb = w.n_blocks
-    diff, total = compare_selection(sel, rp_h, ci_h, w.n_kv_heads, nb, w.sink)
-    say(f"  selection: {diff}/{total} rows differ, all inside the threshold band")
+    diff, total, n_ex = compare_selection(sel, rp_h, ci_h, w.n_kv_heads, nb, w.sink)
+    say(f"  selection: {diff}/{total} rows differ, all inside near-tie bands "
+        f"({n_ex} blocks in such bands)")
     rows = [(g, i) for g in range(w.n_kv_heads) for i in range(nb)]
     if sample_rows is not None and len(rows) > sample_rows:
-        rng = np.random.default_rng(seed)
-        pick = rng.choice(len(rows), size=sample_rows, replace=False)
-        rows = [rows[k] for k in sorted(pick)] + [(0, 0), (w.n_kv_heads - 1, nb - 1)]
+        rows = stratified_rows(w.n_kv_heads, nb, sel.row_ptr, sample_rows, seed)
     # attention on the oracle's CSR
     rp_o, ci_o = csr_to_device(sel.row_ptr, sel.col_idx)
     out_g, lse_g = rbs.blocksparse_attn_fwd(t["q"], t["k"], t["v"], w.block, rp_o, ci_o,

@@ -59,14 +59,19 @@ def test_rag_zero_offsets_is_plain_segment_attention():
 
 
 def test_rag_31k_sampled_rows():
-    """The 20 x 1,536 + 512 RAG layout, 32/8 heads, theta 5e5: sampled
-    passage rows and final-block rows."""
+    """The 20 x 1,536 + 512 RAG layout, 32/8 heads, theta 5e5: in every
+    passage its first two rows, its last row and 12 random rows (300 passage
+    rows), and every other row of the final block plus its last (257 rows)."""
     w = inputs.rag_bf16_31k()
     rng = np.random.default_rng(0)
-    passage_tok = rng.choice(int(w.seg_start[-2]), size=96, replace=False)
-    final_tok = rng.choice(np.arange(int(w.seg_start[-2]), w.seqlen), size=48, replace=False)
-    toks = np.sort(np.concatenate([passage_tok, final_tok, [0, w.seqlen - 1]]))
-    _run(w, tokens=toks)
+    seg = w.seg_start
+    toks = []
+    for p in range(len(seg) - 2):
+        a, b = int(seg[p]), int(seg[p + 1])
+        toks += [a, a + 1, b - 1] + rng.choice(np.arange(a + 2, b - 1), size=12,
+                                               replace=False).tolist()
+    toks += list(range(int(seg[-2]), w.seqlen, 2)) + [w.seqlen - 1]
+    _run(w, tokens=np.unique(np.asarray(toks, np.int64)))
 
 
 def test_rag_split_final_block_all_final_rows():

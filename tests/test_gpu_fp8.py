@@ -2,17 +2,16 @@
 oracle: Q, K, V as E4M3 bytes with per-tensor descales on both sides; the
 oracle decodes them exactly and runs the float64 block-sparse attention.
 
-Tolerance, from the arithmetic. Q.K^T is exact up to fp32 summation (products
-of two E4M3 values fit in fp32), the softmax is fp32, and the one coarse step
-is rounding each probability p to E4M3 (nearest even: relative error <= 2^-4)
-before the P.V product. With weights w_u = p_u / sum p the output error is
-sum_u w_u e_u v_u with |e_u| <= 2^-4, so
-  max-abs  <= 2^-4 * max|v|  (+ bf16 output rounding, 2^-8 * max|out|),
-  mean-abs <= 2^-4 / sqrt(3) * rms(v)   (errors uniform in +-2^-4: their
-             rms, times the weighted rms of v, bounds the mean magnitude).
-Probabilities below 2^-6 round with absolute error <= 2^-10 instead; they
-weigh little and the bounds above hold on these workloads with a margin.
-lse: exact up to fp32 rounding of the scores and of the row sum (1e-3).
+Tolerance, from the arithmetic (fp8_error_model): Q.K^T is exact up to fp32
+summation (products of two E4M3 values fit in fp32), the softmax is fp32, and
+the one coarse step is rounding each probability to E4M3 before it feeds the
+P.V product and the row sum. The model gives, per output element, the
+standard deviation of that rounding noise from the exact softmax weights; the
+mean absolute error must stay within 1.5 times the model's expectation (plus
+the bf16 output rounding) and every element within 8 standard deviations
+plus half a bf16 unit. A systematic slip of a few percent of the keys' weight
+fails the mean. lse: exact up to fp32 rounding of the scores and the row sum
+of rounded P (each normal-range P within 2^-4 relative: 0.07 absolute).
 """
 import math
 
@@ -24,14 +23,10 @@ import block_sparse_long_rbs_amd as rbs
 from block_sparse_long_rbs_amd import device, inputs
 from oracle import rbs_oracle as orc
 
+import fp8_error_model as M
 import gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
-
-
-def _tols(f):
-    v = orc.e4m3_decode(f.v) * f.v_descale
-    return 2.0 ** -4 * float(np.abs(v).max()), 2.0 ** -4 / math.sqrt(3.0) * float(np.sqrt(np.mean(v * v)))
 
 
 def _run(f, t, block, row_ptr, col_idx, **kw):
@@ -42,19 +37,28 @@ def _run(f, t, block, row_ptr, col_idx, **kw):
     return H.to_host(out), lse.cpu().numpy().astype(np.float64)
 
 
-def _compare(w, f, out_g, lse_g, out_o, lse_o, rows, what):
-    tmax, tmean = _tols(f)
-    mx, mean = H._slab_errors(out_g, out_o, rows, w)
-    omax = float(np.nanmax(np.abs(out_o)))
-    H.say(f"  {what}: max-abs {mx:.3e} (bound {tmax + 2 ** -8 * omax:.3e}) "
-          f"mean-abs {mean:.3e} (bound {tmean:.3e})")
-    assert mx <= tmax + 2.0 ** -8 * omax, f"{what}: max-abs {mx}"
-    assert mean <= tmean, f"{what}: mean-abs {mean}"
+def _compare(w, f, out_g, lse_g, out_o, lse_o, rows, what, row_ptr, col_idx):
+    q, k, v = M.decoded(f)
+    sigma = M.rounding_sigma(q, k, v, w.block, row_ptr, col_idx, rows, out_o, lse_o)
+    exact = M.exact_slab(out_o, rows, w.block, w.seqlen, w.group)
+    got = M.exact_slab(out_g, rows, w.block, w.seqlen, w.group)
+    err = got - exact
+    mean, expected, worst = M.check(err, sigma, exact, what)
+    H.say(f"  {what}: {len(rows)} rows, max-abs {np.abs(err).max():.3e}, mean-abs {mean:.3e} "
+          f"(rounding model {expected:.3e}, ratio {mean / expected:.2f}), worst element "
+          f"{worst:.2f} of its allowance")
     G = w.group
+    worst_lse = 0.0
     for g, i in rows:
         t0, t1 = i * w.block, min(w.seqlen, (i + 1) * w.block)
-        d = np.abs(lse_g[g * G:(g + 1) * G, t0:t1] - lse_o[g * G:(g + 1) * G, t0:t1]).max()
-        assert d <= 1e-3, f"{what}: lse row {(g, i)} err {d}"
+        a, b = lse_g[g * G:(g + 1) * G, t0:t1], lse_o[g * G:(g + 1) * G, t0:t1]
+        fin = np.isfinite(b)
+        assert np.array_equal(np.isfinite(a), fin), f"{what}: lse row {(g, i)} finiteness"
+        if fin.any():
+            worst_lse = max(worst_lse, float(np.abs(a[fin] - b[fin]).max()))
+    # every normal-range P rounded up by its most would move lse by ln(1 + 2^-4) = 0.061
+    assert worst_lse <= 0.07, f"{what}: lse err {worst_lse}"
+    H.say(f"  {what}: lse max-abs {worst_lse:.3e}")
 
 
 def test_fp8_ragged_small_all_rows():
@@ -68,7 +72,8 @@ def test_fp8_ragged_small_all_rows():
     out_o, lse_o = orc.blocksparse_attention_fp8(f.q, f.k, f.v, f.q_descale, f.k_descale,
                                                  f.v_descale, w.block, sel.row_ptr, sel.col_idx)
     rows = [(g, i) for g in range(w.n_kv_heads) for i in range(w.n_blocks)]
-    _compare(w, f, out_g, lse_g, out_o, lse_o, rows, "fp8 attention")
+    _compare(w, f, out_g, lse_g, out_o, lse_o, rows, "fp8 attention", sel.row_ptr,
+             sel.col_idx)
 
 
 def test_fp8_last_tile_shorter_than_a_half():
@@ -83,7 +88,8 @@ def test_fp8_last_tile_shorter_than_a_half():
     out_o, lse_o = orc.blocksparse_attention_fp8(f.q, f.k, f.v, f.q_descale, f.k_descale,
                                                  f.v_descale, w.block, sel.row_ptr, sel.col_idx)
     rows = [(g, i) for g in range(w.n_kv_heads) for i in range(w.n_blocks)]
-    _compare(w, f, out_g, lse_g, out_o, lse_o, rows, "fp8 short last tile")
+    _compare(w, f, out_g, lse_g, out_o, lse_o, rows, "fp8 short last tile", sel.row_ptr,
+             sel.col_idx)
 
 
 def test_fp8_descales_scale_exactly():
@@ -122,7 +128,7 @@ def test_fp8_empty_rows_and_skipped_entries():
     rows = [(0, 1), (0, 2), (1, 0), (1, 1), (1, 2)]
     out_o, lse_o = orc.blocksparse_attention_fp8(f.q, f.k, f.v, f.q_descale, f.k_descale,
                                                  f.v_descale, 128, clipped, cols, rows=rows)
-    _compare(w, f, out_g, lse_g, out_o, lse_o, rows, "fp8 edge rows")
+    _compare(w, f, out_g, lse_g, out_o, lse_o, rows, "fp8 edge rows", clipped, cols)
 
 
 def test_fp8_late_dominant_key_raises_the_running_max():
@@ -140,19 +146,21 @@ def test_fp8_late_dominant_key_raises_the_running_max():
     out_g, lse_g = _run(f, t, 128, row_ptr, col_idx)
     out_o, lse_o = orc.blocksparse_attention_fp8(f.q, f.k, f.v, f.q_descale, f.k_descale,
                                                  f.v_descale, 128, row_ptr, col_idx)
-    _compare(w, f, out_g, lse_g, out_o, lse_o, [(0, i) for i in range(4)], "fp8 late key")
+    _compare(w, f, out_g, lse_g, out_o, lse_o, [(0, i) for i in range(4)], "fp8 late key",
+             row_ptr, col_idx)
 
 
 def test_fp8_raise_in_second_half_recomputes_first_half():
     """Every query is 4*e0, so a key's base-2 score is b = 4 k0 scale log2(e)
     and is set by its first coordinate alone. Keys default to b = 0, which
-    fixes the running max at 0 from the first tile. In tile 2, key 300 (first
-    64-key half) sits at b ~ 3, so the first half keeps the max (a lane's
-    share of its row sum is about 8 + 31 < 2^8). Keys 320..383 (second half)
-    sit at b = 4, so every lane's share of the second half's row sum is
-    32 * 16 > 2^8. Rows that see them therefore raise the max in the second
-    half, and the first half's P, already packed, has to be redone from the
-    new max. Every kept probability stays in e4m3's normal range."""
+    fixes the reference at 0 - 3 from the first tile (every P = 8, a lane's
+    share 32 * 8 = 256 <= 448). In tile 2, key 300 (first 64-key half) sits
+    at b ~ 3 (P ~ 64), so the first half keeps the reference (a lane's share
+    is about 64 + 31 * 8 < 448). Keys 320..383 (second half) sit at b = 4
+    (P = 128), so every lane's share of the second half's row sum is
+    32 * 128 > 448. Rows that see them therefore raise the reference in the
+    second half, and the first half's P, already packed, has to be redone from
+    the new one. Every kept probability stays in e4m3's normal range."""
     w = inputs.random_qkv(512, 2, 1, 128, "f32", seed=11, block=128)
     unit = 1.0 / (4.0 / math.sqrt(128) * math.log2(math.e))  # k0 for b = 1
     q = np.zeros_like(w.q)
@@ -175,7 +183,8 @@ def test_fp8_raise_in_second_half_recomputes_first_half():
     out_g, lse_g = _run(f, t, 128, row_ptr, col_idx)
     out_o, lse_o = orc.blocksparse_attention_fp8(f.q, f.k, f.v, f.q_descale, f.k_descale,
                                                  f.v_descale, 128, row_ptr, col_idx)
-    _compare(w, f, out_g, lse_g, out_o, lse_o, [(0, i) for i in range(4)], "fp8 second-half raise")
+    _compare(w, f, out_g, lse_g, out_o, lse_o, [(0, i) for i in range(4)],
+             "fp8 second-half raise", row_ptr, col_idx)
 
 
 @pytest.mark.timeout(600)
@@ -188,15 +197,12 @@ def test_fp8_32k_64_8_heads_sampled_rows():
     _, sel = H.oracle_selection(w)
     t = device.upload_fp8(f)
     out_g, lse_g = _run(f, t, w.block, sel.row_ptr, sel.col_idx)
-    nb = w.n_blocks
-    rng = np.random.default_rng(4)
-    allrows = [(g, i) for g in range(w.n_kv_heads) for i in range(nb)]
-    pick = rng.choice(len(allrows), size=8, replace=False)
-    rows = [allrows[x] for x in sorted(pick)] + [(0, 0), (w.n_kv_heads - 1, nb - 1)]
+    rows = H.stratified_rows(w.n_kv_heads, w.n_blocks, sel.row_ptr, 256, seed=4)
     out_o, lse_o = orc.blocksparse_attention_fp8(f.q, f.k, f.v, f.q_descale, f.k_descale,
                                                  f.v_descale, w.block, sel.row_ptr, sel.col_idx,
                                                  rows=rows)
-    _compare(w, f, out_g, lse_g, out_o, lse_o, rows, "fp8 32K sampled rows")
+    _compare(w, f, out_g, lse_g, out_o, lse_o, rows, "fp8 32K sampled rows", sel.row_ptr,
+             sel.col_idx)
 
 
 @pytest.mark.timeout(600)
@@ -211,10 +217,32 @@ def test_fp8_128k_sampled_rows():
     row_ptr, col_idx = inputs.random_block_csr(w.n_kv_heads, nb, 0.06, seed=9)
     t = device.upload_fp8(f)
     out_g, lse_g = _run(f, t, w.block, row_ptr, col_idx)
-    rng = np.random.default_rng(3)
-    allrows = [(g, i) for g in range(w.n_kv_heads) for i in range(nb)]
-    pick = rng.choice(len(allrows), size=8, replace=False)
-    rows = [allrows[x] for x in sorted(pick)] + [(0, 0), (w.n_kv_heads - 1, nb - 1)]
+    rows = H.stratified_rows(w.n_kv_heads, nb, row_ptr, 256, seed=3)
     out_o, lse_o = orc.blocksparse_attention_fp8(f.q, f.k, f.v, f.q_descale, f.k_descale,
                                                  f.v_descale, w.block, row_ptr, col_idx, rows=rows)
-    _compare(w, f, out_g, lse_g, out_o, lse_o, rows, "fp8 128K sampled rows")
+    _compare(w, f, out_g, lse_g, out_o, lse_o, rows, "fp8 128K sampled rows", row_ptr,
+             col_idx)
+
+
+@pytest.mark.timeout(300)
+def test_fp8_rows_longer_than_the_staged_block_list():
+    """The long-row cases of the bf16 kernel on the fp8 entry: dense causal at
+    40,960 tokens (rows of up to 320 entries) and one 600-entry row with
+    out-of-range entries around list positions 256 and 512 at 65,536 tokens."""
+    for S, seed, hand_built in ((40960, 53, False), (65536, 54, True)):
+        w = inputs.random_qkv(S, 2, 1, 128, "f32", seed=seed, block=128, name=f"fp8_long_{S}")
+        f = inputs.fp8_inputs(w)
+        nb = S // 128
+        if hand_built:
+            (rp, ci), (rpc, cic) = H.long_rows_csr(1, nb, nb - 1, 600, seed=4)
+            rows = [(0, 0), (0, 7), (0, nb - 1)]
+        else:
+            rp, ci = orc.dense_causal_selection(1, nb)
+            rpc, cic = rp, ci
+            rows = [(0, i) for i in (0, 1, 100, 254, 255, 256, 257, 300, nb - 1)]
+        H.say(f"[case] fp8 S={S} longest row {int(np.diff(rp).max())} entries")
+        t = device.upload_fp8(f)
+        out_g, lse_g = _run(f, t, 128, rp, ci)
+        out_o, lse_o = orc.blocksparse_attention_fp8(f.q, f.k, f.v, f.q_descale, f.k_descale,
+                                                     f.v_descale, 128, rpc, cic, rows=rows)
+        _compare(w, f, out_g, lse_g, out_o, lse_o, rows, f"fp8 long rows S={S}", rpc, cic)

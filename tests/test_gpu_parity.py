@@ -26,7 +26,7 @@ def test_tiny_f32_1k():
 
 
 def test_needle_bf16_8k():
-    H.pipeline_case(inputs.needle_bf16_8k(), sample_rows=24)
+    H.pipeline_case(inputs.needle_bf16_8k(), sample_rows=256)
 
 
 def test_mixture_bf16_ragged_small():
@@ -167,3 +167,40 @@ def test_late_dominant_key_raises_the_running_max():
         assert d.max() <= H.TOL_BF16_MAX and d.mean() <= H.TOL_BF16_MEAN, order
         dl = np.abs(lse.cpu().numpy() - lse_o)
         assert dl.max() <= 2e-2, (order, dl.max())
+
+
+@pytest.mark.timeout(300)
+def test_rows_longer_than_the_staged_block_list():
+    """Dense causal attention at 40,960 tokens (320 blocks per row at the end,
+    past the 256 entries the kernel stages in LDS at a time), then one
+    hand-built row of 600 entries at 65,536 tokens: every visible block in a
+    shuffled order with out-of-range entries spliced in around list positions
+    256 and 512. Checked against the oracle on sampled rows, the last row and
+    the rows on both sides of 256 entries."""
+    S, Hq, Hkv, B = 40960, 2, 1, 128
+    w = inputs.random_qkv(S, Hq, Hkv, 128, "bf16", seed=51, block=B, name="dense_40k")
+    H.say(f"[case] dense causal S={S} rows up to {S // B} entries")
+    t = device.upload(w)
+    nb = S // B
+    rp, ci = orc.dense_causal_selection(Hkv, nb)
+    a, b = H.csr_to_device(rp, ci)
+    out, lse = rbs.blocksparse_attn_fwd(t["q"], t["k"], t["v"], B, a, b, want_lse=True)
+    rows = [(0, i) for i in (0, 1, 100, 254, 255, 256, 257, 300, nb - 1)]
+    o, lo = orc.blocksparse_attention(w.q, w.k, w.v, B, rp, ci, rows=rows)
+    mx, mean = H._slab_errors(H.to_host(out), o, rows, w)
+    H._assert_attn(w, mx, mean, "dense 40K sampled rows")
+    toks = H.row_tokens(rows, B, S)
+    assert np.abs(lse.cpu().numpy()[:, toks] - lo[:, toks]).max() <= 2e-2
+
+    S = 65536
+    w = inputs.random_qkv(S, Hq, Hkv, 128, "bf16", seed=52, block=B, name="long_row_64k")
+    nb = S // B
+    (rp, ci), (rpc, cic) = H.long_rows_csr(Hkv, nb, nb - 1, 600, seed=3)
+    H.say(f"[case] one row of {rp[nb] - rp[nb - 1]} entries at S={S}")
+    t = device.upload(w)
+    a, b = H.csr_to_device(rp, ci)
+    out, _ = rbs.blocksparse_attn_fwd(t["q"], t["k"], t["v"], B, a, b)
+    rows = [(0, 0), (0, 7), (0, nb - 1)]
+    o, _ = orc.blocksparse_attention(w.q, w.k, w.v, B, rpc, cic, rows=rows)
+    mx, mean = H._slab_errors(H.to_host(out), o, rows, w)
+    H._assert_attn(w, mx, mean, "600-entry row")

@@ -192,7 +192,7 @@ def test_beta_zero_gives_centroid_only():
         for i in range(w.n_blocks):
             sc = c[g, :i + 1] @ qr[g, i]
             n = orc.budget(i + 1, 0.1)
-            best = sorted(range(i + 1), key=lambda j: (-np.float32(sc[j]), j))[:n]
+            best = sorted(range(i + 1), key=lambda j: (-sc[j], j))[:n]
             assert sel.row(g, i).tolist() == sorted(set(best) | {i})
 
 
