@@ -13,12 +13,16 @@
 //     read from LDS (two 16-byte reads each). The MFMA pairs A and B bytes by
 //     the same (lane half, byte) position, so one common byte order serves
 //     both.
-//   P = 2^(s - m) rounded to e4m3 (nearest even) straight from the score
-//     registers; the row sum adds the same rounded values. The reference m
-//     is kept 3 below the largest score seen when it is set (largest P 8),
-//     which keeps small probabilities out of e4m3's subnormal range; e4m3
-//     tops out at 448 and has no infinity (larger values become NaN), so m is
-//     raised as soon as a lane's share of a half's row sum exceeds 448.
+//   P' = 2^(s - m - e) rounded to e4m3 (nearest even) straight from the
+//     score registers, with one power-of-two exponent e per (query row,
+//     32-key block) chosen so that the block's largest P' lies in (128, 256]:
+//     every block's probabilities use e4m3's whole range (a long tail of small
+//     P is neither pushed into the subnormal range nor flushed to zero by a
+//     large P elsewhere in the row), and the scaled matrix instruction
+//     restores 2^e exactly (its B operand takes one E8M0 exponent per 32-deep
+//     block of each column). The row sum is one more scaled product of the
+//     same bytes with an all-ones operand. The reference m is lazy, as in the
+//     bf16 kernel: raised only when a score passes it by more than 64.
 //   O^T += V^T P^T: per 32-wide slice of the head dim and 64-key half, one
 //     product. The V^T operand comes from 8-bit transposing LDS reads
 //     (ds_read_b64_tr_b8), ordered so that byte j of a lane pairs with the
@@ -28,10 +32,11 @@
 // -> LDS by global_load_lds_dwordx4 with explicit vector-memory counts as in
 // the bf16 kernel (4 loads per wave per tile instead of 8).
 //
-// The softmax's vector instructions, not the matrix products, set the pace,
-// and one wave issues them at a fraction of the SIMD's rate; so the kernel is
-// held to 168 VGPRs (half-tile scores, Q read from LDS) and 49 KB of LDS,
-// which lets three workgroups share a CU (three waves per SIMD).
+// The softmax's vector instructions, not the matrix products, set the pace.
+// The per-block exponents need each block's largest score (a max over the
+// lane's 16 values and one cross-lane exchange) on top of the exponentials;
+// held to 168 VGPRs for three waves per SIMD the kernel spills, so it runs at
+// 229 VGPRs and two waves per SIMD (49 KB of LDS per workgroup).
 //
 // Bound: matrix cores. Algorithmic flops per (query row, key) pair: 4*D.
 
@@ -48,10 +53,21 @@ typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
 
 constexpr int ROW8 = D;  // bytes per K or V row in LDS
 
-// 32x32 block += A (32 x 64, e4m3) * B (64 x 32, e4m3). Zero scale operands
-// select the plain (unscaled) instruction.
+// 32x32 block += A (32 x 64, e4m3) * B (64 x 32, e4m3). Constant zero scale
+// operands select the plain (unscaled) instruction.
 __device__ __forceinline__ f32x16_t mfma_fp8(const v8i_t& a, const v8i_t& b, const f32x16_t& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// The same product with B scaled by E8M0 exponent bytes (2^(sb - 127)), one
+// per 32-deep block of each column. Checked on the GPU with one-wave probes:
+// block 0 of column c is bytes 0-15 of lanes c and c + 32 and takes lane c's
+// byte, block 1 is bytes 16-31 of both and takes lane c + 32's byte; a
+// constant zero operand selects the unscaled instruction, a runtime 0 means
+// 2^-127.
+__device__ __forceinline__ f32x16_t mfma_fp8_bscaled(const v8i_t& a, const v8i_t& b,
+                                                     const f32x16_t& c, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
 }
 
 // 16-byte chunk swizzles in LDS (8 chunks per 128-byte row): chunk c of K row
@@ -102,7 +118,7 @@ __device__ __forceinline__ void dma_tile8(const uint8_t* __restrict__ src, size_
   }
 }
 
-__global__ __launch_bounds__(kThreads, 3) void attn_fp8_kernel(AttnArgs a,
+__global__ __launch_bounds__(kThreads, 2) void attn_fp8_kernel(AttnArgs a,
                                                                const int32_t* __restrict__ row_ptr,
                                                                const int32_t* __restrict__ col_idx,
                                                                float scale_log2, float out_scale) {
@@ -172,6 +188,25 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fp8_kernel(AttnArgs a,
   };
   const char* const qrow = Qs + qq * ROW8;
   const char* const krow = Ks + m32 * ROW8;
+  // Probabilities in e4m3 with one power-of-two scale per 32-key block and
+  // query row. The B operand of the P.V product carries one exponent per
+  // 32-deep block of each column, and the blocks are exactly the key blocks
+  // kb of a half (lanes l and l ^ 32 hold 16 keys of each). So for each key
+  // block the pair takes the largest score, x (base 2, relative to the row's
+  // reference m_run), picks e = ceil(x) - 8 and packs P' = 2^(s - m_run - e),
+  // whose largest value lies in (128, 256]: every block's probabilities use
+  // e4m3's whole range (relative error <= 2^-4 down to 2^-13 of the block's
+  // largest), whatever the other blocks hold, and the product restores 2^e
+  // exactly. The row sum comes from the same scaled bytes, as one more
+  // product with an all-ones A operand.
+  // The reference itself is lazy, as in the bf16 kernel: taken from the
+  // row's first half tile and raised only when a score passes it by more
+  // than 64 (so that sums stay far inside fp32's range). A raise moves it by
+  // a whole number k of powers of two: O and the row sum are multiplied by
+  // 2^-k exactly and a half already packed only needs its exponents lowered
+  // by k, so nothing is recomputed.
+  const v8i_t ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};
   while (j >= 0) {
     const int jn = csr.next(csr.e + 1);
     wait_vmcnt<4>();  // K(j) (and at the first tile Q) has landed; V(j) may be in flight
@@ -181,10 +216,13 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fp8_kernel(AttnArgs a,
     // per-element predicates are not hoisted out of the tile loop
     int t = qq - 4 * hh;
     asm volatile("" : "+v"(t));
-    // P in e4m3, packed as the B operand of the P.V products: byte j of
-    // dword w of key block kb is the lane's score element r = 4 w + j.
+    // P' in e4m3, packed as the B operand of the P.V products: byte j of
+    // dword w of key block kb is the lane's score element r = 4 w + j; sb
+    // holds each half's exponent byte (of key block 2 half in lanes 0-31, of
+    // key block 2 half + 1 in lanes 32-63).
     int pk[4][4];
-    float ls[2];
+    int sb[2];
+    float k_raise = 0.f;
     f32x16_t s[2];
     // S^T = K Q^T for the 64-key half `half` (key blocks 2 half, 2 half + 1),
     // in the order (depth chunk, key block) so that one Q fragment is live
@@ -209,84 +247,69 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fp8_kernel(AttnArgs a,
             if ((2 * half + kk) * 32 + 8 * (r >> 2) + (r & 3) > t) s[kk][r] = -INFINITY;
       }
     };
-    auto half_max = [&]() {
-      float mx = -INFINITY;
+    auto exps = [&](int half) {
+      float mb[2];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+      for (int kk = 0; kk < 2; ++kk) {
+        float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kk][r]);
-      return pair_max(mx) * scale_log2;
-    };
-    auto exps = [&](int half) {
-      const float neg = -m_run;
-      float a0 = 0.f, a1 = 0.f;
+        mb[kk] = pair_max(mx) * scale_log2;  // the key block's largest score
+      }
+      const float hm = fmaxf(mb[0], mb[1]);
+      // reference: the first half's max; later raised by a whole number k of
+      // powers of two when a score passes it by more than 64 (rare; O and
+      // the row sum are rescaled before this tile's products are added, and
+      // the first half's exponents lowered by k)
+      if (first) {
+        m_run = hm;
+        first = false;
+      } else if (__ballot(hm - m_run > 64.f)) {
+        const float k = fmaxf(ceilf(hm - m_run), 0.f);
+        m_run += k;
+        k_raise += k;
+        if (half == 1) sb[0] = max(sb[0] - (int)k, 1);
+      }
+      // block exponent e = ceil(x) - 8, x the block's largest score over the
+      // reference, kept to [-126, 56] (a block whose scores all lie more than
+      // 118 below the reference contributes nothing measurable)
+      float neg[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const float e = ceilf(fminf(fmaxf(mb[kk] - m_run, -118.f), 64.f)) - 8.f;
+        neg[kk] = -(m_run + e);
+        if (kk == hh) sb[half] = (int)e + 127;
+      }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kk][4 * w], scale_log2, neg));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kk][4 * w + 1], scale_log2, neg));
-          const float p2 = __builtin_amdgcn_exp2f(fmaf(s[kk][4 * w + 2], scale_log2, neg));
-          const float p3 = __builtin_amdgcn_exp2f(fmaf(s[kk][4 * w + 3], scale_log2, neg));
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kk][4 * w], scale_log2, neg[kk]));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kk][4 * w + 1], scale_log2, neg[kk]));
+          const float p2 = __builtin_amdgcn_exp2f(fmaf(s[kk][4 * w + 2], scale_log2, neg[kk]));
+          const float p3 = __builtin_amdgcn_exp2f(fmaf(s[kk][4 * w + 3], scale_log2, neg[kk]));
           int xw = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
           xw = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, xw, true);
           pk[2 * half + kk][w] = xw;
-          // the row sum adds the rounded P that the P.V product uses, so the
-          // output stays a weighted mean of V (an overflowed P decodes as NaN)
-          const auto r01 = __builtin_amdgcn_cvt_pk_f32_fp8(xw, false);
-          const auto r23 = __builtin_amdgcn_cvt_pk_f32_fp8(xw, true);
-          a0 += r01[0] + r01[1];
-          a1 += r23[0] + r23[1];
         }
-      ls[half] = a0 + a1;
     };
-    // The reference m_run sits kMaxLift below the largest score seen when it
-    // is set, so that the half tile's largest P is 2^kMaxLift rather than 1:
-    // small probabilities then stay clear of e4m3's subnormal range (below
-    // 2^-6) and of its flush to zero (below 2^-10), which would otherwise
-    // drop the mass of a long tail of small P. It is set from the row's
-    // first half tile and stays while a lane's share of a half's row sum of
-    // rounded P is <= 448 (every P finite in e4m3; an overflow decodes as NaN
-    // and fails the test too); else it is raised to that half's max minus
-    // kMaxLift and O and the row sum are rescaled. After a raise every P of
-    // the half is <= 2^kMaxLift, so a lane's 32 values sum to <= 256 and the
-    // test passes. A raise in the second half recomputes the first half from
-    // K, still in LDS, so every P is rounded once, from its exact exponential.
-    constexpr float kMaxLift = 3.f;
-    auto raise = [&]() {
-      const float m_new = fmaxf(m_run, half_max() - kMaxLift);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+    scores(0);
+    exps(0);
+    scores(1);
+    exps(1);
+    lds_barrier();  // every wave is done with Ks
+    if (jn >= 0) dma_tile8<false>(Kg, rs, a.S, jn * TILE, Ks);
+    if (jn >= 0) wait_vmcnt<4>(); else wait_vmcnt<0>();  // V(j) has landed
+    lds_barrier();
+    if (__ballot(k_raise > 0.f)) {
+      const float alpha = __builtin_amdgcn_exp2f(-k_raise);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    };
-    scores(0);
-    if (first) {
-      m_run = half_max() - kMaxLift;
-      first = false;
     }
-    exps(0);
-    if (__ballot(!(ls[0] <= 448.f))) {
-      raise();
-      exps(0);
-    }
-    scores(1);
-    exps(1);
-    if (__ballot(!(ls[1] <= 448.f))) {
-      raise();
-      exps(1);
-      scores(0);
-      exps(0);
-    }
-    lds_barrier();  // every wave is done with Ks
-    if (jn >= 0) dma_tile8<false>(Kg, rs, a.S, jn * TILE, Ks);
-    l_run += ls[0] + ls[1];
-    if (jn >= 0) wait_vmcnt<4>(); else wait_vmcnt<0>();  // V(j) has landed
-    lds_barrier();
-    // ---- O^T += V^T P^T: fragments read one step ahead ----
+    // ---- O^T += V^T P^T (fragments read one step ahead) and the row sum ----
     __builtin_amdgcn_s_setprio(2);
     auto read_v = [&](int kc, int db, v8i_t& f) {
       const char* vb = Vs + v_lane + (((2 * db + (g16 & 1)) ^ vswz) << 4) + kc * 64 * ROW8;
@@ -299,15 +322,21 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fp8_kernel(AttnArgs a,
     };
     v8i_t vf[2];
     read_v(0, 0, vf[0]);
+    f32x16_t rsum = {};
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       const int kc = st >> 2, db = st & 3;
       if (st < 7) read_v((st + 1) >> 2, (st + 1) & 3, vf[(st + 1) & 1]);
       const v8i_t b = {pk[2 * kc][0], pk[2 * kc][1], pk[2 * kc][2], pk[2 * kc][3],
                        pk[2 * kc + 1][0], pk[2 * kc + 1][1], pk[2 * kc + 1][2], pk[2 * kc + 1][3]};
-      o[db] = mfma_fp8(vf[st & 1], b, o[db]);
+      // every row of this product holds the column sums: element 0 is the
+      // lane's full row sum over the tile's keys
+      if (db == 0) rsum = mfma_fp8_bscaled(ones, b, rsum, sb[kc]);
+      o[db] = mfma_fp8_bscaled(vf[st & 1], b, o[db], sb[kc]);
     }
     __builtin_amdgcn_s_setprio(0);
+    // lanes l and l ^ 32 both hold the full sum; their shares are added at the end
+    l_run += 0.5f * rsum[0];
     lds_barrier();  // every wave is done with Vs
     if (jn >= 0) dma_tile8<true>(Vg, rs, a.S, jn * TILE, Vs);
     j = jn;

@@ -213,13 +213,16 @@ rbs_status blocksparse_attn_fwd_per_head(rbs_dtype dt, const void* q, const void
  * causal masking, softmax_scale and lse); out is bf16 [S][Hq][D], rounded to
  * nearest even.
  * Arithmetic: Q.K^T as fp8 x fp8 matrix-core products summed in fp32; softmax
- * in fp32; the probabilities are rounded to E4M3 (nearest even, relative
- * error <= 2^-4; below 2^-6 of the running maximum an absolute error <= 2^-10
- * instead) and the same rounded values feed both the P.V product and the row
- * sum, so out is a weighted mean of the row's V rows whose weights are within
+ * in fp32; the probabilities are rounded to E4M3 with one power-of-two
+ * scale per (query row, 32-key block), which puts each block's largest in
+ * (128, 256] (nearest even: relative error <= 2^-4 down to 2^-13 of the
+ * block's largest, absolute error <= 2^-17 of it below that), and the same
+ * rounded values feed both the P.V product and the row sum, so out is a
+ * weighted mean of the row's V rows whose weights are within
  * 2^-3 / (1 - 2^-4) relative of the exact softmax weights. Hence
  * |out - exact| <= 0.134 * max over the row's keys of |v_descale * v[u] - exact|
- * up to the small-probability term, fp32 and bf16 rounding.
+ * up to the small-probability term, fp32 and bf16 rounding; lse is the log
+ * of that rounded row sum (within ln(1 + 2^-4) of the exact one).
  * Supported: head_dim 128 and block 128 (else RBS_E_UNSUPPORTED); group CSR
  * rows g * nb + i as rbs_select writes them.
  * Errors: RBS_E_ARG (also for a descale that is not finite and > 0),

@@ -10,8 +10,9 @@ standard deviation of that rounding noise from the exact softmax weights; the
 mean absolute error must stay within 1.5 times the model's expectation (plus
 the bf16 output rounding) and every element within 8 standard deviations
 plus half a bf16 unit. A systematic slip of a few percent of the keys' weight
-fails the mean. lse: exact up to fp32 rounding of the scores and the row sum
-of rounded P (each normal-range P within 2^-4 relative: 0.07 absolute).
+fails the mean. lse is the log of the same rounded row sum (each probability within 2^-4
+relative: 0.07 absolute), which keeps (out, lse) pairs consistent when
+partial results are merged.
 """
 import math
 
@@ -56,7 +57,7 @@ def _compare(w, f, out_g, lse_g, out_o, lse_o, rows, what, row_ptr, col_idx):
         assert np.array_equal(np.isfinite(a), fin), f"{what}: lse row {(g, i)} finiteness"
         if fin.any():
             worst_lse = max(worst_lse, float(np.abs(a[fin] - b[fin]).max()))
-    # every normal-range P rounded up by its most would move lse by ln(1 + 2^-4) = 0.061
+    # every probability rounded up by its most would move lse by ln(1 + 2^-4) = 0.061
     assert worst_lse <= 0.07, f"{what}: lse err {worst_lse}"
     H.say(f"  {what}: lse max-abs {worst_lse:.3e}")
 
@@ -132,15 +133,20 @@ def test_fp8_empty_rows_and_skipped_entries():
 
 
 def test_fp8_late_dominant_key_raises_the_running_max():
-    """A key far above the first tile's scores (2^8 past its max) takes the
-    rescale path; P stays inside E4M3's range and the result matches."""
+    """A key more than 64 (base 2) above the first tile's scores for the
+    queries of the last block: the kernel raises its reference by a whole
+    number of powers of two and rescales the partial output (its rare path)."""
     w = inputs.random_qkv(512, 2, 1, 128, "f32", seed=8, block=128)
     q = w.q.copy()
     k = w.k.copy()
-    k[300, 0] = 3.0 * q[400, 0] / np.linalg.norm(q[400, 0]) * math.sqrt(128)
+    k[300, 0] = 5.0 * q[400, 0] / np.linalg.norm(q[400, 0]) * math.sqrt(128)
     w.q, w.k = q, k
     H.say("[case] fp8 late dominant key S=512")
     f = inputs.fp8_inputs(w)
+    qd = orc.e4m3_decode(f.q[:, 0]) * f.q_descale
+    kd = orc.e4m3_decode(f.k[:, 0]) * f.k_descale
+    b = kd @ qd[400] / math.sqrt(128) * math.log2(math.e)
+    assert b[300] - b[:64].max() > 64      # the raise path is taken
     row_ptr, col_idx = orc.dense_causal_selection(1, 4)
     t = device.upload_fp8(f)
     out_g, lse_g = _run(f, t, 128, row_ptr, col_idx)
@@ -150,25 +156,23 @@ def test_fp8_late_dominant_key_raises_the_running_max():
              row_ptr, col_idx)
 
 
-def test_fp8_raise_in_second_half_recomputes_first_half():
+def test_fp8_raise_in_second_half_lowers_the_first_halfs_exponents():
     """Every query is 4*e0, so a key's base-2 score is b = 4 k0 scale log2(e)
     and is set by its first coordinate alone. Keys default to b = 0, which
-    fixes the reference at 0 - 3 from the first tile (every P = 8, a lane's
-    share 32 * 8 = 256 <= 448). In tile 2, key 300 (first 64-key half) sits
-    at b ~ 3 (P ~ 64), so the first half keeps the reference (a lane's share
-    is about 64 + 31 * 8 < 448). Keys 320..383 (second half) sit at b = 4
-    (P = 128), so every lane's share of the second half's row sum is
-    32 * 128 > 448. Rows that see them therefore raise the reference in the
-    second half, and the first half's P, already packed, has to be redone from
-    the new one. Every kept probability stays in e4m3's normal range."""
+    fixes the reference at 0 from the first tile. In tile 2, key 300 (first
+    64-key half) sits at b ~ 0.5, so the first half keeps the reference and
+    is packed against it. Keys 320..383 (second half) sit at b = 70, more
+    than 64 above, so rows that see them raise the reference by 70 in the
+    second half: the first half, already packed, only has its block
+    exponents lowered by 70 and O is rescaled before the tile's products."""
     w = inputs.random_qkv(512, 2, 1, 128, "f32", seed=11, block=128)
     unit = 1.0 / (4.0 / math.sqrt(128) * math.log2(math.e))  # k0 for b = 1
     q = np.zeros_like(w.q)
     q[:, :, 0] = 4.0
     k = w.k.copy()
     k[:, :, 0] = 0.0
-    k[300, 0, 0] = 3.0 * unit
-    k[320:384, 0, 0] = 4.0 * unit
+    k[300, 0, 0] = 0.5 * unit
+    k[320:384, 0, 0] = 70.0 * unit
     w.q, w.k = q, k
     H.say("[case] fp8 raise in the second half S=512")
     f = inputs.fp8_inputs(w)
@@ -177,7 +181,7 @@ def test_fp8_raise_in_second_half_recomputes_first_half():
     kd = orc.e4m3_decode(f.k[:, 0]) * f.k_descale
     b = kd @ qd[400] / math.sqrt(128) * math.log2(math.e)
     assert np.all(b[:300] == 0) and np.all(b[301:320] == 0) and np.all(b[384:] == 0)
-    assert 2.5 < b[300] < 3.5 and np.allclose(b[320:384], 4.0, atol=1e-6)
+    assert 0.3 < b[300] < 0.7 and np.allclose(b[320:384], 70.0, atol=1e-4)
     row_ptr, col_idx = orc.dense_causal_selection(1, 4)
     t = device.upload_fp8(f)
     out_g, lse_g = _run(f, t, 128, row_ptr, col_idx)
