@@ -22,6 +22,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "rbs.h")
 RBS_OK, RBS_E_ARG, RBS_E_UNSUPPORTED, RBS_E_CAPACITY, RBS_E_HIP = range(5)
 RBS_DT_BF16, RBS_DT_F32 = 0, 1
 RBS_SEL_FORCE_SINK = 0x1
+RBS_SELECT_STATIC_SCRATCH_BYTES = 16 << 20   # the header's static scratch size
 
 _c_i32, _c_u32, _c_i64, _c_f32, _c_f64 = (ctypes.c_int32, ctypes.c_uint32, ctypes.c_int64,
                                           ctypes.c_float, ctypes.c_double)
@@ -35,6 +36,8 @@ _SIGS = {
                                   _c_u32, _vp, _vp, _vp, _c_i64, _vp,
                                   ctypes.POINTER(ctypes.c_size_t), _vp]),
     "rbs_select_capacity": (_c_i64, [_c_i32, _c_i32, _c_f64, _c_f64, _c_u32]),
+    "rbs_select_static": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_f64,
+                                         _c_f64, _c_u32, _vp, _vp, _vp, _c_i64, _vp]),
     "rbs_block_stats_per_head": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _c_i32, _c_i32, _c_i32,
                                                 _c_i32, _c_i32, _vp, _vp, _vp, _vp, _vp]),
     "rbs_select_per_head": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
@@ -223,6 +226,41 @@ def rbs_select(cen, rad, qrep, qnorm, keep_ratio_centroid: float, keep_ratio_res
         cen.data_ptr(), rad.data_ptr(), qrep.data_ptr(), qnorm.data_ptr(), _ptr(beta), Hkv, nb, D,
         keep_ratio_centroid, keep_ratio_rescue, flags, _ptr(beta_out), row_ptr.data_ptr(),
         col_idx.data_ptr(), cap, workspace.data_ptr(), ctypes.byref(wsz), _stream(cen)))
+    return row_ptr, col_idx, beta_out
+
+
+def rbs_select_static(cen, rad, qrep, qnorm, keep_ratio_centroid: float,
+                      keep_ratio_rescue: float, sink: bool = False,
+                      beta: Optional[torch.Tensor] = None, want_beta: bool = False,
+                      row_ptr: Optional[torch.Tensor] = None,
+                      col_idx: Optional[torch.Tensor] = None,
+                      beta_out: Optional[torch.Tensor] = None):
+    """rbs_select with the library's static scratch instead of a workspace
+    (the call itself allocates no device memory). Outputs may be passed in
+    (row_ptr [Hkv*nb+1], col_idx [capacity] int32, beta_out [Hkv,nb] fp32), so
+    that nothing is allocated here either; otherwise they are allocated."""
+    fn = "rbs_select_static"
+    Hkv, nb, D = cen.shape
+    dev = cen.device
+    for name, t, shape in (("cen", cen, (Hkv, nb, D)), ("rad", rad, (Hkv, nb)),
+                           ("qrep", qrep, (Hkv, nb, D)), ("qnorm", qnorm, (Hkv, nb)),
+                           ("beta", beta, (Hkv, nb)), ("beta_out", beta_out, (Hkv, nb))):
+        if t is not None:
+            _check_tensor(fn, name, t, shape, torch.float32, dev)
+    cap = rbs_select_capacity(Hkv, nb, keep_ratio_centroid, keep_ratio_rescue, sink)
+    if row_ptr is None:
+        row_ptr = torch.empty(Hkv * nb + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    _check_csr(fn, row_ptr, col_idx, Hkv * nb, dev)
+    if want_beta and beta_out is None:
+        beta_out = torch.empty((Hkv, nb), dtype=torch.float32, device=dev)
+    _need_cuda(cen, rad, qrep, qnorm, beta, row_ptr, col_idx, beta_out)
+    flags = RBS_SEL_FORCE_SINK if sink else 0
+    _check(fn, lib().rbs_select_static(
+        cen.data_ptr(), rad.data_ptr(), qrep.data_ptr(), qnorm.data_ptr(), _ptr(beta), Hkv, nb, D,
+        keep_ratio_centroid, keep_ratio_rescue, flags, _ptr(beta_out), row_ptr.data_ptr(),
+        col_idx.data_ptr(), col_idx.numel(), _stream(cen)))
     return row_ptr, col_idx, beta_out
 
 

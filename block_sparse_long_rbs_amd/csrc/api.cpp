@@ -256,6 +256,30 @@ rbs_status rbs_select(const float* k_centroid, const float* k_radius, const floa
                        row_ptr, col_idx, col_capacity, workspace, workspace_bytes, stream);
 }
 
+rbs_status rbs_select_static(const float* k_centroid, const float* k_radius,
+                             const float* q_rep, const float* q_rep_norm, const float* beta_in,
+                             int32_t n_kv_heads, int32_t n_blocks, int32_t head_dim,
+                             double keep_ratio_centroid, double keep_ratio_rescue,
+                             uint32_t flags, float* beta_out, int32_t* row_ptr,
+                             int32_t* col_idx, int64_t col_capacity, void* stream) {
+  // size check first: a call that needs more scratch than the array holds
+  // fails before anything device-side is touched
+  size_t need = 0;
+  rbs_status st = select_common(nullptr, nullptr, nullptr, nullptr, nullptr, n_kv_heads,
+                                n_kv_heads, n_blocks, head_dim, keep_ratio_centroid,
+                                keep_ratio_rescue, flags, nullptr, nullptr, nullptr, 0, nullptr,
+                                &need, nullptr);
+  if (st != RBS_OK) return st;
+  if (need > RBS_SELECT_STATIC_SCRATCH_BYTES) return RBS_E_CAPACITY;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  st = static_scratch(as_stream(stream), &ws, &ws_bytes);
+  if (st != RBS_OK) return st;
+  return select_common(k_centroid, k_radius, q_rep, q_rep_norm, beta_in, n_kv_heads, n_kv_heads,
+                       n_blocks, head_dim, keep_ratio_centroid, keep_ratio_rescue, flags,
+                       beta_out, row_ptr, col_idx, col_capacity, ws, &ws_bytes, stream);
+}
+
 rbs_status rbs_select_per_head(const float* k_centroid, const float* k_radius,
                                const float* q_rep_head, const float* q_rep_head_norm,
                                const float* beta_in, int32_t n_q_heads, int32_t n_kv_heads,

@@ -69,6 +69,9 @@ struct SelectArgs {
   int sink;
 };
 rbs_status launch_select(const SelectArgs& a, hipStream_t st);
+// Device address and size of rbs_select_static's scratch array on the GPU
+// that runs stream st (the current GPU for the null stream).
+rbs_status static_scratch(hipStream_t st, void** ptr, size_t* bytes);
 
 struct AttnArgs {
   const void* q;

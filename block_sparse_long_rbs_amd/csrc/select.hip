@@ -19,6 +19,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "rbs_common.h"
 
 namespace rbs {
@@ -552,6 +554,35 @@ int select_rows_per_group(int nb, int D) {
 
 size_t select_score_workspace(int H, int nb) {
   return nb <= kTriMaxBlocks ? (size_t)H * (tri_off(nb) + nb) * sizeof(float) : 0;
+}
+
+// Scratch of rbs_select_static: a file-scope device array, so that the call
+// allocates nothing. Each GPU holds its own copy until the process ends;
+// host code uses only the per-device address hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[RBS_SELECT_STATIC_SCRATCH_BYTES];
+
+rbs_status static_scratch(hipStream_t st, void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int cur = 0, dev = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return RBS_E_HIP;
+  dev = cur;
+  if (st && hipStreamGetDevice(st, &dev) != hipSuccess) return RBS_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return RBS_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // the array's address on this device, taken with the device current
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return RBS_E_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return RBS_E_HIP;
+    if (e != hipSuccess || !p) return RBS_E_HIP;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = RBS_SELECT_STATIC_SCRATCH_BYTES;
+  return RBS_OK;
 }
 
 rbs_status launch_select(const SelectArgs& a, hipStream_t st) {

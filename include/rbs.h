@@ -123,6 +123,27 @@ rbs_status rbs_select(const float* k_centroid, const float* k_radius, const floa
                       int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                       void* workspace, size_t* workspace_bytes, void* stream);
 
+/*
+ * rbs_select_static - rbs_select without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. It calls no allocator; its
+ * scratch is a static device array of RBS_SELECT_STATIC_SCRATCH_BYTES per GPU,
+ * held from the first call on that GPU until the process ends. Arguments,
+ * outputs and errors as rbs_select, minus workspace/workspace_bytes; a call
+ * whose workspace (as rbs_select's size query reports it) exceeds the array
+ * returns RBS_E_CAPACITY and enqueues nothing. The GPU is the one that runs
+ * `stream` (the current GPU for the null stream). Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (several streams or
+ * host threads at once) race and must be serialised by the caller.
+ */
+#define RBS_SELECT_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+rbs_status rbs_select_static(const float* k_centroid, const float* k_radius,
+                             const float* q_rep, const float* q_rep_norm, const float* beta_in,
+                             int32_t n_kv_heads, int32_t n_blocks, int32_t head_dim,
+                             double keep_ratio_centroid, double keep_ratio_rescue,
+                             uint32_t flags, float* beta_out, int32_t* row_ptr,
+                             int32_t* col_idx, int64_t col_capacity, void* stream);
+
 /* Number of col_idx entries rbs_select may write for these arguments (host
  * only, no device work): Hkv * sum_i min(i+1, n_c(i) + n_r(i) + 1 + sink).
  * For rbs_select_per_head pass n_q_heads as the first argument (one list per

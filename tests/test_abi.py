@@ -223,3 +223,20 @@ def test_sizes_beyond_the_supported_range_are_refused(L):
     assert stats(L, **big) == E.RBS_E_UNSUPPORTED
     assert attn(L, **big) == E.RBS_E_UNSUPPORTED
     assert bmask(L, seg=(0, 2 ** 30), rer=(0,), **big) == E.RBS_E_UNSUPPORTED
+
+
+def test_select_static_refuses_on_the_host(L):
+    """The no-allocation selection entry checks its arguments and the size of
+    its static scratch before touching the device; the binding's copy of the
+    scratch size equals the header's."""
+    import re
+    with open(_lib.HEADER) as f:
+        m = re.search(r"#define RBS_SELECT_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.RBS_SELECT_STATIC_SCRATCH_BYTES
+    s = L.rbs_select_static
+    assert s(P, P, P, P, None, 4, 64, 128, 0.0, 0.1, 0, None, P, P, 1 << 20, None) == E.RBS_E_ARG
+    assert s(P, P, P, P, None, 4, 64, 80, 0.1, 0.1, 0, None, P, P, 1 << 20, None) \
+        == E.RBS_E_UNSUPPORTED
+    # one list per query head at 128K needs far more scratch than the array holds
+    assert s(P, P, P, P, None, 32, 1024, 128, 0.03, 0.03, 0, None, P, P, 1 << 24, None) \
+        == E.RBS_E_CAPACITY
