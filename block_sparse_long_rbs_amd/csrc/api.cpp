@@ -109,9 +109,10 @@ rbs_status select_common(const float* k_centroid, const float* k_radius, const f
   select_sizes(n_blocks, keep_ratio_centroid, keep_ratio_rescue, sink, &per_head, &widest);
   const int64_t rows = (int64_t)n_row_heads * n_blocks;
   const size_t counts_bytes = align256((size_t)rows * 4);
+  const size_t partial_bytes = align256((size_t)((rows + 63) / 64) * 4);
   const size_t lists_bytes = align256((size_t)rows * widest * 4);
   const size_t scores_bytes = align256(select_score_workspace(n_row_heads, n_blocks));
-  const size_t need = 256 + counts_bytes + lists_bytes + scores_bytes;
+  const size_t need = 256 + counts_bytes + partial_bytes + lists_bytes + scores_bytes;
   if (!workspace) {
     *workspace_bytes = need;
     return RBS_OK;
@@ -133,10 +134,11 @@ rbs_status select_common(const float* k_centroid, const float* k_radius, const f
   a.beta_out = beta_out;
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
-  a.counts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 256);
-  a.lists = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 256 + counts_bytes);
-  a.scores = reinterpret_cast<float*>(static_cast<char*>(workspace) + 256 + counts_bytes +
-                                      lists_bytes);
+  char* const ws = static_cast<char*>(workspace);
+  a.counts = reinterpret_cast<int32_t*>(ws + 256);
+  a.partial = reinterpret_cast<int32_t*>(ws + 256 + counts_bytes);
+  a.lists = reinterpret_cast<int32_t*>(ws + 256 + counts_bytes + partial_bytes);
+  a.scores = reinterpret_cast<float*>(ws + 256 + counts_bytes + partial_bytes + lists_bytes);
   a.rbeta = a.scores + (size_t)n_row_heads * ((size_t)n_blocks * (n_blocks + 1) / 2);
   a.H = n_row_heads;
   a.G = n_row_heads / n_kv_heads;

@@ -57,6 +57,7 @@ struct SelectArgs {
   int32_t* row_ptr;
   int32_t* col_idx;
   int32_t* counts;   // workspace: [H*nb]
+  int32_t* partial;  // workspace: [ceil(H*nb / 64)] count sums per 64 rows
   int32_t* lists;    // workspace: [H*nb][stride]
   float* scores;     // workspace: packed triangular centroid scores per row head (nb <= 1024)
   float* rbeta;      // workspace: r_j * beta_j per KV head (nb <= 1024)

@@ -16,6 +16,8 @@
 // fixed-stride workspace slot with its count.
 // Kernel 2 (compact): exclusive scan of the counts into row_ptr and a copy of
 // each row into col_idx.
+// Launches are XCD-aware: a head's work items run on a fixed subset of the
+// eight XCDs, so its statistics and score rows stay in those XCDs' L2.
 
 #include <math.h>
 
@@ -108,15 +110,49 @@ __host__ __device__ __forceinline__ size_t tri_off(int i) { return (size_t)i * (
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+// Work item (head g, item t) of a launch whose T items per head are spread so
+// that each head's items run on a fixed subset of the eight XCDs (workgroup
+// x runs on XCD x % 8): the head's statistics and score rows are then
+// fetched into one or two XCDs' L2 instead of all eight. Returns false for
+// padding workgroups.
+__device__ __forceinline__ bool xcd_item(int x, int H, int T, int& g, int& t) {
+  const int xcd = x & 7, s = x >> 3;
+  if (H % 8 == 0) {                 // H / 8 heads per XCD
+    g = xcd + 8 * (s / T);
+    t = s % T;
+    return g < H;
+  }
+  if (8 % H == 0) {                 // 8 / H XCDs per head, items interleaved
+    const int reps = 8 / H;
+    g = xcd % H;
+    t = s * reps + xcd / H;
+    return t < T;
+  }
+  g = x / T;                        // any other head count: plain order
+  t = x % T;
+  return g < H;
+}
+
+__host__ __forceinline__ int xcd_grid(int H, int T) {
+  if (H % 8 == 0) return H * T;
+  if (8 % H == 0) return 8 * ((T + 8 / H - 1) / (8 / H));
+  return H * T;
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void score_tiles_kernel(SelectArgs a) {
-  const int g = blockIdx.y;       // row head
-  const int gk = g / a.G;          // its KV head
   const int nb = a.nb;
   const int nt = (nb + kTile - 1) / kTile;
   const int ntiles = nt * (nt + 1) / 2;
+  int g, item;                     // row head, tile (ntiles: the rescue-coefficient item)
+  if (!xcd_item(blockIdx.x, a.H, ntiles + 1, g, item)) return;
+  const int gk = g / a.G;          // its KV head
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if ((int)blockIdx.x >= ntiles) {
+  if (item >= ntiles) {
+    // row head 0's item also clears the per-64-row count sums that the row
+    // kernel (which runs after this kernel) accumulates
+    if (g == 0 && a.partial)
+      for (int x = tid; x < (a.H * nb + 63) / 64; x += kThreads) a.partial[x] = 0;
     // rescue coefficients of KV head gk (once, from its first row head):
     // beta = clamp((r - mean) / (max - mean), 0, 1)
     __shared__ float red[8];
@@ -152,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void score_tiles_kernel(SelectArgs a) {
     return;
   }
   // tile index -> (row tile ti, column tile tj <= ti), heaviest rows first
-  int t = blockIdx.x;
+  int t = item;
   int ti = nt - 1;
   while (t > ti) { t -= ti + 1; --ti; }
   const int tj = t;
@@ -283,7 +319,7 @@ __device__ __forceinline__ uint32_t nth_largest_small(const uint32_t (&key)[M], 
 
 // One row (g, i): its i + 1 candidates, M per lane (64 M >= i + 1).
 template <int M>
-__device__ __forceinline__ void select_row(const SelectArgs& a, int g, int i, uint32_t* buf) {
+__device__ __forceinline__ int select_row(const SelectArgs& a, int g, int i, uint32_t* buf) {
   const int nb = a.nb;
   const int lane = threadIdx.x & 63;
   const int nvis = i + 1;
@@ -321,21 +357,47 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, int g, int i, ui
     if (sel && pos < a.stride) out[pos] = j;
     base += __popcll(msk);
   }
-  if (lane == 0) a.counts[(size_t)g * nb + i] = min(base, a.stride);
+  const int n = min(base, a.stride);
+  if (lane == 0) a.counts[(size_t)g * nb + i] = n;
+  return n;
 }
 
 __global__ __launch_bounds__(kThreads) void select_rows_kernel(SelectArgs a) {
   __shared__ uint32_t cand[kThreads / 64][64 * kSelM];
   const int nb = a.nb;
   const int wave = threadIdx.x >> 6;
-  // 4 rows per workgroup, all of one KV head; heaviest rows first
+  // 4 rows per workgroup, all of one row head, on that head's XCDs;
+  // heaviest rows first
   const int rows_per_g = (nb + 3) / 4;
-  const int g = blockIdx.x / rows_per_g;
-  const int i = nb - 1 - ((blockIdx.x % rows_per_g) * 4 + wave);
-  if (i < 0) return;
-  if (i < 4 * 64) select_row<4>(a, g, i, cand[wave]);
-  else if (i < 8 * 64) select_row<8>(a, g, i, cand[wave]);
-  else select_row<kSelM>(a, g, i, cand[wave]);
+  int g, item;
+  if (!xcd_item(blockIdx.x, a.H, rows_per_g, g, item)) return;
+  const int i = nb - 1 - (item * 4 + wave);
+  int n = 0;
+  if (i >= 0) {
+    if (i < 4 * 64) n = select_row<4>(a, g, i, cand[wave]);
+    else if (i < 8 * 64) n = select_row<8>(a, g, i, cand[wave]);
+    else n = select_row<kSelM>(a, g, i, cand[wave]);
+  }
+  // the workgroup's row counts go into the per-64-row sums with one atomic
+  // per 64-row group touched (the four rows are consecutive)
+  __shared__ int wc[4];
+  if ((threadIdx.x & 63) == 0) wc[wave] = n;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int grp = -1, acc = 0;
+    for (int w = 3; w >= 0; --w) {   // ascending rows
+      const int iw = nb - 1 - (item * 4 + w);
+      if (iw < 0) continue;
+      const int gr = (int)(((size_t)g * nb + iw) >> 6);
+      if (gr != grp) {
+        if (grp >= 0 && acc) atomicAdd(a.partial + grp, acc);
+        grp = gr;
+        acc = 0;
+      }
+      acc += wc[w];
+    }
+    if (grp >= 0 && acc) atomicAdd(a.partial + grp, acc);
+  }
 }
 
 constexpr int kLongRows = 8;  // query blocks per workgroup on the long-row path
@@ -471,6 +533,8 @@ __global__ __launch_bounds__(kThreads) void select_long_kernel(SelectArgs a, int
 
 // CSR assembly: one workgroup per 16 rows. The row offsets are the sum of all
 // earlier counts plus a scan inside the group; the copies are independent.
+// The sum of all earlier counts is taken from the per-64-row sums when the
+// row kernel produced them (partial != null), else from the counts.
 constexpr int kCompactRows = 16;
 
 __device__ __forceinline__ int wave_isum(int x) {
@@ -480,6 +544,7 @@ __device__ __forceinline__ int wave_isum(int x) {
 }
 
 __global__ __launch_bounds__(kThreads) void compact_kernel(const int32_t* __restrict__ counts,
+                                                           const int32_t* __restrict__ partial,
                                                            const int32_t* __restrict__ lists,
                                                            int stride, int nrows,
                                                            int32_t* __restrict__ row_ptr,
@@ -492,7 +557,10 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(const int32_t* __rest
   const int nr = min(kCompactRows, nrows - r0);
   // sum of the counts of all earlier rows
   int s = 0;
-  for (int x = tid; x < r0; x += kThreads) s += counts[x];
+  const int c0 = partial ? (r0 & ~63) : 0;   // earlier rows summed from the counts
+  if (partial)
+    for (int x = tid; x < (r0 >> 6); x += kThreads) s += partial[x];
+  for (int x = c0 + tid; x < r0; x += kThreads) s += counts[x];
   s = wave_isum(s);
   if (lane == 0) wsum[wave] = s;
   __syncthreads();
@@ -592,7 +660,7 @@ rbs_status launch_select(const SelectArgs& a, hipStream_t st) {
   }
   if (a.nb <= kTriMaxBlocks) {
     const int nt = (a.nb + kTile - 1) / kTile;
-    dim3 g1(nt * (nt + 1) / 2 + 1, a.H);
+    dim3 g1(xcd_grid(a.H, nt * (nt + 1) / 2 + 1));
     if (a.D == 64)
       hipLaunchKernelGGL(score_tiles_kernel<64>, g1, dim3(kThreads), 0, st, a);
     else
@@ -600,7 +668,8 @@ rbs_status launch_select(const SelectArgs& a, hipStream_t st) {
     rbs_status s = launch_status();
     if (s != RBS_OK) return s;
     const int rows_per_g = (a.nb + 3) / 4;
-    hipLaunchKernelGGL(select_rows_kernel, dim3(rows_per_g * a.H), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(select_rows_kernel, dim3(xcd_grid(a.H, rows_per_g)), dim3(kThreads), 0, st,
+                       a);
   } else {
     const int R = select_rows_per_group(a.nb, a.D);
     if (R <= 0) return RBS_E_UNSUPPORTED;
@@ -612,9 +681,11 @@ rbs_status launch_select(const SelectArgs& a, hipStream_t st) {
   rbs_status s = launch_status();
   if (s != RBS_OK) return s;
   const int nrows = a.H * a.nb;
+  // the per-64-row sums exist on the score-tile path (its kernel clears them)
+  const int32_t* partial = a.nb <= kTriMaxBlocks ? a.partial : nullptr;
   hipLaunchKernelGGL(compact_kernel, dim3((nrows + kCompactRows - 1) / kCompactRows),
-                     dim3(kThreads), 0, st, a.counts, a.lists, a.stride, nrows, a.row_ptr,
-                     a.col_idx);
+                     dim3(kThreads), 0, st, a.counts, partial, a.lists, a.stride, nrows,
+                     a.row_ptr, a.col_idx);
   return launch_status();
 }
 
