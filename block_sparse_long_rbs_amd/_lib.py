@@ -48,6 +48,9 @@ _SIGS = {
                                                      _vp, _vp, _vp]),
     "blocksparse_attn_fwd": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
                                             _c_i32, _c_i32, _vp, _vp, _c_f32, _vp, _vp, _vp]),
+    "blocksparse_attn_fwd_shared_query": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _c_i32,
+                                                         _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp,
+                                                         _c_f32, _vp, _vp, _vp]),
     "blocksparse_attn_fwd_fp8": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                                 _c_i32, _vp, _vp, _c_f32, _c_f32, _c_f32, _c_f32,
                                                 _vp, _vp, _vp]),
@@ -337,6 +340,29 @@ def blocksparse_attn_fwd(q, k, v, block: int, row_ptr, col_idx, softmax_scale: f
         out = torch.empty_like(q)
     lse = torch.empty((Hq, S), dtype=torch.float32, device=q.device) if want_lse else None
     _check("blocksparse_attn_fwd", lib().blocksparse_attn_fwd(
+        _dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), S, Hq, Hkv, D, block,
+        row_ptr.data_ptr(), col_idx.data_ptr(), softmax_scale, out.data_ptr(), _ptr(lse),
+        _stream(q)))
+    return out, lse
+
+
+def blocksparse_attn_fwd_shared_query(q, k, v, block: int, row_ptr, col_idx,
+                                      softmax_scale: float = 0.0, want_lse: bool = False,
+                                      out: Optional[torch.Tensor] = None):
+    """blocksparse_attn_fwd with neighbouring query blocks processed together
+    over the union of their block lists (same result) -> (out, lse or None)."""
+    fn = "blocksparse_attn_fwd_shared_query"
+    _check_qkv(fn, q, k, v)
+    S, Hq, D = q.shape
+    Hkv = k.shape[1]
+    _check_csr(fn, row_ptr, col_idx, Hkv * -(-S // block), q.device)
+    if out is not None:
+        _check_tensor(fn, "out", out, q.shape, q.dtype, q.device)
+    _need_cuda(q, k, v, row_ptr, col_idx, out)
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((Hq, S), dtype=torch.float32, device=q.device) if want_lse else None
+    _check(fn, lib().blocksparse_attn_fwd_shared_query(
         _dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), S, Hq, Hkv, D, block,
         row_ptr.data_ptr(), col_idx.data_ptr(), softmax_scale, out.data_ptr(), _ptr(lse),
         _stream(q)))

@@ -320,6 +320,22 @@ rbs_status blocksparse_attn_fwd_fp8(const void* q, const void* k, const void* v,
   return launch_attn_fp8_csr(a, q_descale, k_descale, v_descale, as_stream(stream));
 }
 
+rbs_status blocksparse_attn_fwd_shared_query(rbs_dtype dt, const void* q, const void* k,
+                                             const void* v, int32_t seqlen, int32_t n_q_heads,
+                                             int32_t n_kv_heads, int32_t head_dim, int32_t block,
+                                             const int32_t* row_ptr, const int32_t* col_idx,
+                                             float softmax_scale, void* out, float* lse,
+                                             void* stream) {
+  if (dt != RBS_DT_BF16 && dt != RBS_DT_F32) return RBS_E_ARG;
+  AttnArgs a;
+  const rbs_status st = attn_args(q, k, v, seqlen, n_q_heads, n_kv_heads, head_dim, block, row_ptr,
+                                  col_idx, softmax_scale, out, lse, false, a);
+  if (st != RBS_OK) return st;
+  if (dt != RBS_DT_BF16 || head_dim != 128 || block != 128) return RBS_E_UNSUPPORTED;
+  if (seqlen == 0) return RBS_OK;
+  return launch_attn_bf16_pairs(a, as_stream(stream));
+}
+
 rbs_status blocksparse_attn_fwd_per_head(rbs_dtype dt, const void* q, const void* k,
                                          const void* v, int32_t seqlen, int32_t n_q_heads,
                                          int32_t n_kv_heads, int32_t head_dim, int32_t block,

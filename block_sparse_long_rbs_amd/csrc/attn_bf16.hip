@@ -59,19 +59,20 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_ca
 // rows); lane l of a load lands at base + 16 l, so each lane fetches the
 // logical chunk that the swizzle puts there. Rows past the sequence end
 // repeat the last row (finite values; their scores are masked).
-template <bool IS_V>
+template <bool IS_V, int NW = 4>
 __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, size_t rs, int S,
                                          int key0, char* lds) {
+  constexpr int kLoads = 32 / NW;  // 1 KB loads (4 rows) per wave
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r4 = lane >> 4, pc = lane & 15;
-  const uint32_t dst = lds_u32(lds) + wave * 8 * 1024;
-  const int row0 = key0 + wave * 32;
+  const uint32_t dst = lds_u32(lds) + wave * kLoads * 1024;
+  const int row0 = key0 + wave * 4 * kLoads;
   const uint32_t rsb = (uint32_t)rs * 2;  // bytes per token row
-  if (row0 + 32 <= S) {
+  if (row0 + 4 * kLoads <= S) {
     const uint16_t* base = src + (size_t)row0 * rs;
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
+    for (int it = 0; it < kLoads; ++it) {
       const int lc = IS_V ? (pc ^ (r4 << 2)) : (pc ^ (((it & 3) << 2) | r4));
       dma16(base + (size_t)(it * 4) * rs, r4 * rsb + lc * 16, dst + it * 1024);
     }
@@ -80,7 +81,7 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, size_
     const int r0 = min(row0, S - 1);
     const uint16_t* cbase = src + (size_t)r0 * rs;
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
+    for (int it = 0; it < kLoads; ++it) {
       const int lc = IS_V ? (pc ^ (r4 << 2)) : (pc ^ (((it & 3) << 2) | r4));
       const int tok = min(row0 + it * 4 + r4, S - 1);
       dma16(cbase, (uint32_t)(tok - r0) * rsb + lc * 16, dst + it * 1024);
@@ -89,8 +90,8 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, size_
 }
 
 __device__ __forceinline__ void load_q(const uint16_t* __restrict__ Q, int S, int Hq, int h,
-                                       int qt, bf16x8_t* qf) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+                                       int qt, int wave, bf16x8_t* qf) {
+  const int lane = threadIdx.x & 63;
   const int t = qt * TILE + wave * 32 + (lane & 31);
   const int hh = lane >> 5;
 #pragma unroll
@@ -191,27 +192,76 @@ __device__ __forceinline__ int segment_of_tile(const SegArgs& s, int tile) {
   return lo;
 }
 
-template <bool SEG>
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
-                                                                const int32_t* __restrict__ row_ptr,
-                                                                const int32_t* __restrict__ col_idx,
-                                                                SegArgs seg, float scale_log2) {
+// Key tiles of a pair unit (shared-query mode): the merged walk over two CSR
+// rows, those of query tiles qt[0] and qt[1] of one head, each staged in LDS
+// 256 entries at a time. Every wave evaluates the walk identically, so list
+// reloads (which need a workgroup barrier) happen in step. A tile listed in
+// both rows is visited once with both halves members; entries outside
+// 0..qt[h] are skipped; unsorted rows are walked correctly (each half visits
+// exactly its own entries), sorted rows share every common tile.
+struct PairTiles {
+  const int32_t* col_idx;
+  int e[2], e1[2], cb[2], qt[2], cur[2];
+  int* lst;
+  __device__ int head(int h) {
+    for (; e[h] < e1[h]; ++e[h]) {
+      if (e[h] - cb[h] >= kThreads) {  // reload: every wave reaches this point together
+        lds_barrier();
+        cb[h] = e[h];
+        if (threadIdx.x < kThreads)
+          lst[h * kThreads + threadIdx.x] =
+              (cb[h] + (int)threadIdx.x < e1[h]) ? col_idx[cb[h] + threadIdx.x] : -1;
+        lds_barrier();
+      }
+      const int j = lst[h * kThreads + e[h] - cb[h]];
+      if (j >= 0 && j <= qt[h]) return j;
+    }
+    return -1;
+  }
+  // the walk's next tile (-1 at the end) and which halves list it
+  __device__ int next(bool& m0, bool& m1) {
+    const int a0 = cur[0], a1 = cur[1];
+    const int j = a0 < 0 ? a1 : (a1 < 0 ? a0 : min(a0, a1));
+    m0 = j >= 0 && a0 == j;
+    m1 = j >= 0 && a1 == j;
+    if (m0) { ++e[0]; cur[0] = head(0); }
+    if (m1) { ++e[1]; cur[1] = head(1); }
+    return j;
+  }
+};
+
+// The kernel body. PAIR (shared-query execution): one workgroup of 8 waves
+// takes query tiles 2p and 2p + 1 of one head, one 4-wave half each, and
+// walks the union of their block lists: each key tile is moved into LDS once
+// for both halves, and a half skips the products of a tile its own list does
+// not hold.
+template <bool SEG, bool PAIR>
+__device__ __forceinline__ void attn_bf16_body(const AttnArgs& a,
+                                               const int32_t* __restrict__ row_ptr,
+                                               const int32_t* __restrict__ col_idx,
+                                               const SegArgs& seg, float scale_log2) {
+  constexpr int NW = PAIR ? 8 : 4;  // waves per workgroup
   __shared__ __attribute__((aligned(1024))) char Ks[TILE * ROWB];
   __shared__ __attribute__((aligned(1024))) char Vs[TILE * ROWB];
-  __shared__ int lst[SEG ? 1 : kThreads];
+  __shared__ int lst[SEG ? 1 : (PAIR ? 2 * kThreads : kThreads)];
   const int G = a.Hq / a.Hkv;
   const int nq = (a.S + TILE - 1) / TILE;
   // segment mode: workgroups [0, grid_split) run key-range chunks
   const bool chunked = SEG && (int)blockIdx.x < seg.grid_split;
   Unit u;
-  if (!SEG) {
+  if (PAIR) {
+    if (!decode_unit(blockIdx.x, G, a.Hkv, 0, (nq + 1) / 2, 1, u)) return;
+  } else if (!SEG) {
     if (!decode_unit(blockIdx.x, G, a.Hkv, 0, nq, 1, u)) return;
   } else if (chunked) {
     if (!decode_unit(blockIdx.x, G, a.Hkv, seg.qt_lo, seg.qt_hi, seg.chunks, u)) return;
   } else {
     if (!decode_unit(blockIdx.x - seg.grid_split, G, a.Hkv, seg.rest_lo, seg.rest_hi, 1, u)) return;
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = (threadIdx.x >> 6) & 3;       // the wave's 32-row slot in its query tile
+  const int hq = PAIR ? (int)(threadIdx.x >> 8) : 0;  // pair mode: the wave's half
+  const int qt_me = PAIR ? 2 * u.qt + hq : u.qt;  // the wave's query tile
   const int m32 = lane & 31, hh = lane >> 5;
   const size_t rs = (size_t)a.Hkv * D;
   const uint16_t* Kg = static_cast<const uint16_t*>(a.k) + (size_t)u.g * D;
@@ -219,8 +269,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
 
   // tile iteration state
   CsrTiles csr{col_idx, 0, 0, 0, u.qt, lst};
+  PairTiles pt;
+  if (PAIR) {
+    pt.col_idx = col_idx;
+    pt.lst = lst;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      pt.qt[h] = 2 * u.qt + h;
+      const int row = (a.per_head ? u.h : u.g) * nq + pt.qt[h];
+      pt.e[h] = pt.qt[h] < nq ? row_ptr[row] : 0;
+      pt.e1[h] = pt.qt[h] < nq ? row_ptr[row + 1] : 0;
+      pt.cb[h] = pt.e[h];
+    }
+    const int hl = threadIdx.x >> 8, tl = threadIdx.x & (kThreads - 1);
+    lst[threadIdx.x] = (pt.e[hl] + tl < pt.e1[hl]) ? col_idx[pt.e[hl] + tl] : -1;
+    lds_barrier();
+    pt.cur[0] = pt.head(0);
+    pt.cur[1] = pt.head(1);
+  }
   int jseg_lo = 0;
-  if (!SEG) {
+  if (!SEG && !PAIR) {
     const int row = (a.per_head ? u.h : u.g) * nq + u.qt;
     csr.e = row_ptr[row];
     csr.e1 = row_ptr[row + 1];
@@ -240,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
   }
 
   bf16x8_t qf[8];
-  if (!SEG) load_q(static_cast<const uint16_t*>(a.q), a.S, a.Hq, u.h, u.qt, qf);
+  if (!SEG) load_q(static_cast<const uint16_t*>(a.q), a.S, a.Hq, u.h, qt_me, wave, qf);
   f32x16_t o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = (f32x16_t){};
@@ -255,7 +323,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
   const int qq = wave * 32 + m32;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  int j = SEG ? jseg_lo : csr.next(csr.e);
+  bool mem0 = true, mem1 = true;  // pair mode: which halves list tile j
+  int j = SEG ? jseg_lo : (PAIR ? pt.next(mem0, mem1) : csr.next(csr.e));
   if (SEG) {
     // The Q tile goes to LDS by DMA (into Vs, which is free until the first
     // V tile) together with the first K tile, so the two land in one memory
@@ -275,20 +344,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
   } else {
     wait_vmcnt<0>();  // Q fragments and the CSR chunk are in registers before any tile DMA
     if (j >= 0) {
-      dma_tile<false>(Kg, rs, a.S, j * TILE, Ks);
-      dma_tile<true>(Vg, rs, a.S, j * TILE, Vs);
+      dma_tile<false, NW>(Kg, rs, a.S, j * TILE, Ks);
+      dma_tile<true, NW>(Vg, rs, a.S, j * TILE, Vs);
     }
   }
   while (j >= 0) {
-    const int jn = SEG ? segt.next_after(j) : csr.next(csr.e + 1);
-    wait_vmcnt<8>();  // K(j) has landed (V(j) may still be in flight)
+    bool mn0 = false, mn1 = false;
+    const int jn = SEG ? segt.next_after(j) : (PAIR ? pt.next(mn0, mn1) : csr.next(csr.e + 1));
+    // pair mode: a half computes only on the tiles its own list holds (the
+    // test is uniform over the half's waves; barriers stay outside it)
+    const bool me = !PAIR || (hq ? mem1 : mem0);
+    wait_vmcnt<32 / NW>();  // K(j) has landed (V(j) may still be in flight)
     lds_barrier();
+    f32x16_t s[4];
+    if (me) {
     // ---- S^T = K Q^T (four independent accumulators in turn) ----
     // Wave priority: matrix phases win issue over the other workgroup's
     // softmax on the same SIMD (P.V highest, so a tile's output accumulation
     // is not held up behind the next tile's scores).
     __builtin_amdgcn_s_setprio(1);
-    f32x16_t s[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) s[kb] = (f32x16_t){};
 #pragma unroll
@@ -308,10 +382,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __builtin_amdgcn_s_setprio(0);
+    }
     lds_barrier();  // every wave is done with Ks
-    if (jn >= 0) dma_tile<false>(Kg, rs, a.S, jn * TILE, Ks);
+    if (jn >= 0) dma_tile<false, NW>(Kg, rs, a.S, jn * TILE, Ks);
+    uint32_t pk[4][8];
+    if (me) {
     // ---- online softmax (base 2) ----
-    if (j == u.qt) {
+    if (j == qt_me) {
       // causal mask inside the diagonal tile; t is made opaque so that the
       // per-element predicates are not hoisted out of the tile loop
       int t = qq - 4 * hh;
@@ -337,7 +414,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
       m_run = tile_max();
       first = false;
     }
-    uint32_t pk[4][8];
     auto exps = [&]() {
       const float neg = -m_run;
       float ls = 0.f;
@@ -366,8 +442,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
       ls = exps();
     }
     l_run += ls;
-    if (jn >= 0) wait_vmcnt<8>(); else wait_vmcnt<0>();  // V(j) has landed
+    }
+    if (jn >= 0) wait_vmcnt<32 / NW>(); else wait_vmcnt<0>();  // V(j) has landed
     lds_barrier();
+    if (me) {
     // ---- O^T += V^T P^T (four independent accumulators in turn) ----
     __builtin_amdgcn_s_setprio(2);
 #pragma unroll
@@ -394,17 +472,34 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __builtin_amdgcn_s_setprio(0);
+    }
     lds_barrier();  // every wave is done with Vs
-    if (jn >= 0) dma_tile<true>(Vg, rs, a.S, jn * TILE, Vs);
+    if (jn >= 0) dma_tile<true, NW>(Vg, rs, a.S, jn * TILE, Vs);
     j = jn;
+    mem0 = mn0;
+    mem1 = mn1;
   }
   if (chunked)
     store_part(seg.part + ((((size_t)(u.qt - seg.qt_lo) * a.Hq + u.h) * seg.chunks + u.c) * TILE) *
                               kPartRow,
                o, m_run, l_run);
-  else
-    store_out_lds(static_cast<uint16_t*>(a.out), a.lse, a.S, a.Hq, u.h, u.qt,
-                  SEG ? seg.q_row_begin : 0, o, m_run, l_run, 1.0f, Ks);
+  else if (!PAIR || qt_me < nq)
+    store_out_lds(static_cast<uint16_t*>(a.out), a.lse, a.S, a.Hq, u.h, qt_me,
+                  SEG ? seg.q_row_begin : 0, o, m_run, l_run, 1.0f, hq ? Vs : Ks, wave);
+}
+
+template <bool SEG>
+__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a,
+                                                                const int32_t* __restrict__ row_ptr,
+                                                                const int32_t* __restrict__ col_idx,
+                                                                SegArgs seg, float scale_log2) {
+  attn_bf16_body<SEG, false>(a, row_ptr, col_idx, seg, scale_log2);
+}
+
+__global__ __launch_bounds__(2 * kThreads, 1) void attn_bf16_pair_kernel(
+    AttnArgs a, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+    SegArgs seg, float scale_log2) {
+  attn_bf16_body<false, true>(a, row_ptr, col_idx, seg, scale_log2);
 }
 
 }  // namespace
@@ -430,6 +525,26 @@ rbs_status launch_attn_bf16_csr(const AttnArgs& a, hipStream_t st) {
   none.part = nullptr;
   hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3(attn_grid(a.Hq, a.Hkv, nq, 1)), dim3(kThreads),
                      0, st, a, a.row_ptr, a.col_idx, none, scale_log2);
+  return launch_status();
+}
+
+rbs_status launch_attn_bf16_pairs(const AttnArgs& a, hipStream_t st) {
+  const float scale_log2 = a.scale * 1.4426950408889634f;
+  const int nq = (a.S + TILE - 1) / TILE;
+  SegArgs none;
+  none.n_seg = 0;
+  none.q_row_begin = 0;
+  none.theta = 0.f;
+  none.qt_lo = 0;
+  none.qt_hi = nq;
+  none.chunks = 0;
+  none.chunk_tiles = 0;
+  none.rest_lo = 0;
+  none.rest_hi = nq;
+  none.grid_split = 0;
+  none.part = nullptr;
+  hipLaunchKernelGGL(attn_bf16_pair_kernel, dim3(attn_grid(a.Hq, a.Hkv, (nq + 1) / 2, 1)),
+                     dim3(2 * kThreads), 0, st, a, a.row_ptr, a.col_idx, none, scale_log2);
   return launch_status();
 }
 

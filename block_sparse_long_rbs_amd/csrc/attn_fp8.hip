@@ -342,7 +342,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_kernel(AttnArgs a,
     j = jn;
   }
   store_out_lds(static_cast<uint16_t*>(a.out), a.lse, a.S, a.Hq, u.h, u.qt, 0, o, m_run, l_run,
-                out_scale, KVs);
+                out_scale, KVs, wave);
 }
 
 }  // namespace

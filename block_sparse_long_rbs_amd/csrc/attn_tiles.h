@@ -94,7 +94,8 @@ __device__ __forceinline__ bool decode_unit(int x, int G, int Hkv, int qt_lo, in
 
 // Normalised output of one query tile (bf16, O / l times out_scale) and the
 // row's log-sum-exp (natural log; -inf for a row that saw no key), through
-// LDS (buf: 32 KB, 16-byte aligned, free when called): each lane writes its
+// LDS (buf: 32 KB, 16-byte aligned, free when called; `wave` = the wave's
+// 32-row slot in the tile): each lane writes its
 // 4-value groups into its row (16-byte chunks swizzled by row), then each
 // wave reads back its own 32 rows as whole 16-byte chunks, so that the stores
 // to O cover 256 contiguous bytes per row instead of 8 bytes of 64 different
@@ -102,8 +103,8 @@ __device__ __forceinline__ bool decode_unit(int x, int G, int Hkv, int qt_lo, in
 __device__ __forceinline__ void store_out_lds(uint16_t* __restrict__ O, float* __restrict__ lse,
                                               int S, int Hq, int h, int qt, int row_begin,
                                               const f32x16_t* o, float m_run, float l_run,
-                                              float out_scale, char* buf) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+                                              float out_scale, char* buf, int wave) {
+  const int lane = threadIdx.x & 63;
   const int m32 = lane & 31, hh = lane >> 5;
   const float l = pair_sum(l_run);
   const float inv = l > 0.f ? out_scale / l : 0.f;

@@ -87,6 +87,9 @@ struct AttnArgs {
   int per_head;   // CSR rows per query head (h * nb + i) instead of per KV head (g * nb + i)
 };
 rbs_status launch_attn_bf16_csr(const AttnArgs& a, hipStream_t st);
+// Shared-query execution: neighbouring query tiles 2p and 2p + 1 of a head in
+// one 8-wave workgroup over the union of their block lists.
+rbs_status launch_attn_bf16_pairs(const AttnArgs& a, hipStream_t st);
 // fp8 (e4m3) Q, K, V with per-tensor dequantisation factors; bf16 output.
 rbs_status launch_attn_fp8_csr(const AttnArgs& a, float q_descale, float k_descale,
                                float v_descale, hipStream_t st);

@@ -10,6 +10,8 @@
  *            Selection: Centroid Base + Rescue Branch"
  *   [BA]     "Block-Attention for Efficient Prefilling"
  *            (paperlayer.ai/abs/2409.15355v5)
+ *   [QUILT]  "QUILT: Rethinking Sparse-Attention Prefill through Shared Query
+ *            Execution" (newx.sg)
  *
  * Conventions shared by every call
  * --------------------------------
@@ -213,6 +215,30 @@ rbs_status blocksparse_attn_fwd(rbs_dtype dt, const void* q, const void* k, cons
                                 int32_t head_dim, int32_t block, const int32_t* row_ptr,
                                 const int32_t* col_idx, float softmax_scale, void* out,
                                 float* lse, void* stream);
+
+/*
+ * blocksparse_attn_fwd_shared_query - blocksparse_attn_fwd computed with
+ * neighbouring query blocks processed together.
+ *
+ * [QUILT] "QUILT: Rethinking Sparse-Attention Prefill through Shared Query
+ * Execution" (newx.sg), "Abstract" and "Innovation": neighbouring queries
+ * select overlapping KV entries, so processing them jointly loads each
+ * shared entry once. Here query blocks 2p and 2p + 1 of one query head run
+ * in one workgroup over the union of their CSR rows: a key block listed in
+ * both rows is moved into on-chip memory once and used by both, a block in
+ * one row only by that row's queries. The result is blocksparse_attn_fwd's
+ * definition and its arithmetic, unchanged (bit-identical output and lse for
+ * the same CSR); only the execution order differs. Rows may be in any order
+ * (ascending rows, as rbs_select writes them, share every common block).
+ * Supported: bf16 with head_dim 128 and block 128 (else RBS_E_UNSUPPORTED);
+ * group CSR rows g * nb + i. Arguments and errors as blocksparse_attn_fwd.
+ */
+rbs_status blocksparse_attn_fwd_shared_query(rbs_dtype dt, const void* q, const void* k,
+                                             const void* v, int32_t seqlen, int32_t n_q_heads,
+                                             int32_t n_kv_heads, int32_t head_dim, int32_t block,
+                                             const int32_t* row_ptr, const int32_t* col_idx,
+                                             float softmax_scale, void* out, float* lse,
+                                             void* stream);
 
 /* Per-query-head block lists (see rbs_select_per_head): row h * nb + i. */
 rbs_status blocksparse_attn_fwd_per_head(rbs_dtype dt, const void* q, const void* k,

@@ -240,3 +240,21 @@ def test_select_static_refuses_on_the_host(L):
     # one list per query head at 128K needs far more scratch than the array holds
     assert s(P, P, P, P, None, 32, 1024, 128, 0.03, 0.03, 0, None, P, P, 1 << 24, None) \
         == E.RBS_E_CAPACITY
+
+
+def test_shared_query_validation(L):
+    f = L.blocksparse_attn_fwd_shared_query
+    ok = dict(dt=0, q=P, k=P, v=P, S=1024, Hq=8, Hkv=2, D=128, B=128, rp=P, ci=P, sc=0.0, o=P)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["dt"], a["q"], a["k"], a["v"], a["S"], a["Hq"], a["Hkv"], a["D"], a["B"],
+                 a["rp"], a["ci"], a["sc"], a["o"], None, None)
+    assert call(dt=1) == E.RBS_E_UNSUPPORTED       # fp32: the vector-ALU path has no pair mode
+    assert call(D=64) == E.RBS_E_UNSUPPORTED
+    assert call(B=64) == E.RBS_E_UNSUPPORTED
+    assert call(q=PM) == E.RBS_E_ARG
+    assert call(Hq=7) == E.RBS_E_ARG
+    assert call(dt=5) == E.RBS_E_ARG
+    assert call(S=0) == E.RBS_OK
