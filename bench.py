@@ -82,7 +82,8 @@ def main():
     G = Hq // Hkv
     nb = w.n_blocks
     cap = rbs.rbs_select_capacity(Hkv, nb, w.keep_ratio_centroid, w.keep_ratio_rescue, w.sink)
-    ws = torch.empty(1 << 22, dtype=torch.uint8, device="cuda")
+    # the select workspace (about 9.5 MB at this size), allocated once outside the timed steps
+    ws = torch.empty(16 << 20, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(t["q"])
 
     def step():
@@ -180,6 +181,9 @@ def main():
             "stats_hbm_frac": round(stats_bytes / (t_stats * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "stats_select_hbm_frac": round((stats_bytes + select_bytes) /
                                            ((t_stats + t_sel) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "select_gbs": round(select_bytes / (t_sel * 1e-3) / 1e9, 1),
+            "select_hbm_frac": round(select_bytes / (t_sel * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "select_bound": "latency (three dependent kernels over ~5 MB; not HBM bound)",
             "stats_bytes": stats_bytes, "select_bytes": select_bytes,
             "percentiles_ms": {n: {"p10": round(float(np.percentile(v, 10)), 4),
                                    "median": round(float(np.median(v)), 4),
@@ -219,6 +223,21 @@ def main():
         }
         log(f"dense causal attention {t_dense:.2f} ms -> speedup {t_dense / t_attn:.2f}x")
         del rpd_t, cid_t
+        # shared-query execution (neighbouring query blocks over the union of
+        # their lists) on the step's own lists, against the standard entry
+        for _ in range(2):
+            rbs.blocksparse_attn_fwd_shared_query(t["q"], t["k"], t["v"], B, rp, ci, out=out)
+        e0.record(stream)
+        for _ in range(5):
+            rbs.blocksparse_attn_fwd_shared_query(t["q"], t["k"], t["v"], B, rp, ci, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_sq = e0.elapsed_time(e1) / 5
+        result["shared_query_execution"] = {
+            "attn_ms": round(t_sq, 4), "tflops": round(flops / (t_sq * 1e-3) / 1e12, 1),
+            "time_over_standard_entry": round(t_sq / t_attn, 3),
+            "note": "same lists and result; query blocks 2p, 2p+1 share key tiles in one workgroup"}
+        log(f"shared-query execution {t_sq:.3f} ms ({t_sq / t_attn:.2f}x the standard entry)")
         # per-query-head selection (the other reading of the representative
         # query): one block list per query head, same keep ratios
         wsh = torch.empty(96 << 20, dtype=torch.uint8, device="cuda")
@@ -368,7 +387,8 @@ def cpu_baseline(w, flops_total, n_rows, log):
                 if p.get("user_api") == "blas"]
     except ImportError:
         blas = []
-    cores = max([n for _, n in blas if n] or [len(os.sched_getaffinity(0))])
+    host_cores = len(os.sched_getaffinity(0))
+    cores = max([n for _, n in blas if n] or [host_cores])
     t0 = time.perf_counter()
     c, r, qr, qn = orc.block_stats(w.q, w.k, w.n_kv_heads, w.block)
     t_stats = time.perf_counter() - t0
@@ -402,7 +422,10 @@ def cpu_baseline(w, flops_total, n_rows, log):
     val = flops_total / t_total / 1e12
     log(f"cpu oracle: stats {t_stats:.1f}s select {t_sel:.1f}s attention sample {t_attn_sample:.1f}s "
         f"-> {t_total:.0f}s per layer ({val:.4f} TFLOP/s)")
-    return {"value": round(val, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    return {"value": round(val, 6), "unit": "TFLOP/s", "cores": cores, "host_cores": host_cores,
+            "cores_note": "cores = BLAS threads the oracle ran with; host_cores = CPUs in the "
+                          "process's affinity set",
+            "kind": "oracle",
             "sample": (f"float64 NumPy oracle on the same 128K inputs: block stats and selection "
                        f"over all {w.n_kv_heads * nb} rows ({t_stats:.1f}s + {t_sel:.1f}s), "
                        f"attention on {n_rows} random (KV head, query block) rows "
