@@ -92,3 +92,16 @@ def test_rag_split_final_block_all_final_rows():
     ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
     _run(w, tokens=toks, workspace=ws)
     _run(w, q_row_begin=s_last + 37, tokens=np.arange(s_last + 37, w.seqlen), workspace=ws)
+
+
+def test_rag_mixed_passage_lengths_from_inside_a_passage():
+    """Passages of 128, 512, 384 and 896 tokens and a ragged 300-token final
+    block, re-rotation offsets unrelated to the segment starts, theta 1e4;
+    every row from inside the second passage (not on a tile boundary) to the
+    end, and none before it written."""
+    S = 128 + 512 + 384 + 896 + 300
+    w = inputs.random_qkv(S, 8, 2, 128, "bf16", seed=35, block=128, name="rag_mixed")
+    w.seg_start = np.array([0, 128, 640, 1024, 1920, S], np.int32)
+    w.k_rerotate = np.array([0, 50, 700, 12, 0], np.int32)
+    w.rope_theta = 1e4
+    _run(w, q_row_begin=128 + 77)
